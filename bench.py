@@ -1,0 +1,206 @@
+"""Engram forward throughput on one MI355X.
+
+One step = one engram_forward call over one batch of the workload (hash +
+gather, K/V projection, gate, short conv + residual), inputs resident in HBM.
+Prints one JSON line: tokens/s, per-kernel times from HIP events recorded
+inside the timed region on the launch stream, the roofline of the dominant
+kernel, and the oracle's single-thread CPU rate on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b4_t1024]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Engram forward tokens/sec at 1 MI355X; gather/gate HBM GB/s as % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+
+
+def kernel_model(w, N):
+    """Algorithmic work per launch of each kernel: (bound, amount, unit).
+    Bytes count what the method must move (rows, ids, activations, outputs),
+    not re-reads; the GEMM counts its multiply-adds as 2 flops."""
+    s = 2 if w.dtype == "bf16" else 4
+    E, d, hc = w.emb_dim, w.hidden, w.hc_mult
+    return {
+        "hash_gather": ("hbm", N * (4 + 2 * E * s), "B"),
+        "project_gemm": ("mfma" if w.dtype == "bf16" else "alu", 2.0 * N * E * (hc + 1) * d, "FLOP"),
+        "gate": ("hbm", N * (2 * hc * d * s + 4 * hc), "B"),
+        "short_conv": ("hbm", N * (d * s + 4 * hc + hc * d * s), "B"),
+        "advance_state": ("hbm", 0, "B"),
+    }
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (the runtime torch loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The oracle (single-threaded C, double precision) over a prefix of sequence 0."""
+    import numpy as np
+
+    import oracle as orc
+
+    T = inp.seq_total
+    ids0 = inp.ids[:1]
+    o_all = orc.Oracle.from_workload(w, inp, batch=1, seqlen=T)
+    idx = o_all.hash(ids0, remap=inp.remap).reshape(T, -1)
+    off = np.concatenate([[0], np.cumsum(inp.primes)[:-1]])
+    wkv, gk, gq, cw = inp.wkv(), inp.gamma_k(), inp.gamma_q(), inp.conv_w()
+
+    def run(n):
+        rows = np.unique((idx[:n] + off).ravel())
+        tab = inp.table_rows(rows)
+        hid = inp.hidden_at(np.zeros(n, np.int64), np.arange(n))
+        o = o_all.with_shape(1, n)
+        pos = np.arange(n)
+        t0 = time.perf_counter()
+        o.forward_at(ids0[:, :n], inp.remap, tab, wkv, gk, gq, cw, hid.reshape(n, -1), pos, table_keys=rows,
+                     hidden_keys=pos)
+        return time.perf_counter() - t0
+
+    n0 = min(8, T)
+    t_small = run(n0)
+    n = int(min(T, max(n0, budget_s / max(t_small / n0, 1e-9))))
+    dt = run(n) if n > n0 else t_small
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full forward over the first {n} positions of sequence 0 of {w.name} "
+                      f"({dt:.1f} s single-threaded, no BLAS)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="b4_t1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Engram tables of every workload fit in one MI355X's HBM, so this "
+              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import engram_synth as S
+    import hashed_gram_conditional_amd as eg
+    from engram_synth.device import device_inputs
+
+    w = S.WORKLOADS[args.config]
+    if w.decode_prompt:
+        print("decode-shaped workloads are measured with --config of a prefill shape", file=sys.stderr)
+        sys.exit(2)
+    inp = S.Inputs(w)
+    torch.cuda.set_device(0)
+    d = device_inputs(inp)
+    cfg = eg.EngramConfig.make(**w.config_kwargs(inp))
+    p = eg.Params(remap=d["remap"], tables=d["tables"], w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                  conv_w=d["conv_w"])
+    ws = eg.alloc_workspace(cfg)
+    out = torch.empty((w.batch, w.seqlen, w.hc_mult, w.hidden), dtype=d["hidden"].dtype, device="cuda")
+    names = eg.kernel_names(cfg)
+    nk = len(names)
+    N = w.batch * w.seqlen
+
+    for _ in range(args.warmup):
+        eg.forward(cfg, p, d["ids"], d["hidden"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; each kernel bracketed by HIP events on the launch stream
+    hip = Hip()
+    evs = [hip.events(2 * nk) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        eg.forward(cfg, p, d["ids"], d["hidden"], out=out, workspace=ws, stream=stream, events=evs[k])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    per_kernel_ms = [sum(hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs) / args.steps for i in range(nk)]
+    step_gpu_ms = sum(hip.elapsed_ms(e[0], e[-1]) for e in evs) / args.steps
+    for e in evs:
+        hip.destroy(e)
+
+    ms_per_step = dt * 1e3 / args.steps
+    model = kernel_model(w, N)
+    kernels = []
+    for name, ms in zip(names, per_kernel_ms):
+        bound, amount, unit = model[name]
+        if unit == "FLOP":
+            ach = amount / (ms * 1e-3) / 1e12
+            peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else FP32_PEAK_TFLOPS
+            u = "TFLOP/s"
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            peak, u = HBM_PEAK_GBS, "GB/s"
+        kernels.append({"name": name, "avg_us": round(ms * 1e3, 2), "bound": bound, "achieved": round(ach, 1),
+                        "peak": peak, "unit": u, "frac": round(ach / peak, 4), "work_per_launch": amount})
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f).get(w.name, {}).get(dom["name"])
+        if tr is not None:
+            traffic = tr
+    roofline = {"kernel": dom["name"], "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
+    hbm = [k for k in kernels if k["bound"] == "hbm" and k["work_per_launch"] > 0]
+    hbm_bytes = sum(k["work_per_launch"] for k in hbm)
+    hbm_us = sum(k["avg_us"] for k in hbm)
+    hbm_path = {"kernels": [k["name"] for k in hbm], "achieved": round(hbm_bytes / (hbm_us * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm_bytes / (hbm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    res = {
+        "metric": METRIC, "value": round(N / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "vocab": w.vocab,
+                   "orders": w.orders, "heads_per_order": w.heads_per_order, "head_dim": w.head_dim,
+                   "hidden": w.hidden, "hc_mult": w.hc_mult, "table_rows": w.table_rows,
+                   "tokens_per_step": N, "parallelism": "single-gpu"},
+        "gpu_ms_per_step_events": round(step_gpu_ms, 4),
+        "roofline": roofline, "gather_gate_conv_hbm": hbm_path, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -227,6 +227,15 @@ class Workload:
     def tokens_per_call(self) -> int:
         return self.batch * self.seqlen
 
+    def config_kwargs(self, inputs: "Inputs", batch: Optional[int] = None, seqlen: Optional[int] = None) -> dict:
+        """Keyword arguments describing this workload's layer and call shape."""
+        return dict(batch=self.batch if batch is None else batch, seqlen=self.seqlen if seqlen is None else seqlen,
+                    vocab=self.vocab, orders=list(self.orders), heads_per_order=self.heads_per_order,
+                    head_dim=self.head_dim, hidden=self.hidden, hc_mult=self.hc_mult,
+                    multipliers=[int(m) for m in inputs.multipliers], primes=[int(p) for p in inputs.primes],
+                    conv_kernel=self.conv_kernel, conv_dilation=self.conv_dilation, pad_id=self.pad_id,
+                    dtype=self.dtype, norm_eps=self.norm_eps, gate_clamp=self.gate_clamp)
+
     def replace(self, **kw) -> "Workload":
         d = dataclasses.asdict(self)
         d.update(kw)

@@ -16,7 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libengram_synth.so")
 SRC_PATH = os.path.join(_HERE, "csrc", "synth_fill.hip")
 
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17", "-ffp-contract=off",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-shared", "-std=c++17",
+               "-ffp-contract=off",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -66,3 +67,42 @@ def fill(tensor, seed: int, stream_id: int, sigma: float, bias: float = 0.0, bas
                                 base, float(ih4_scale(sigma)), float(bias), dt, ctypes.c_void_p(stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill_ih4 failed with hipError {rc}")
+
+
+def device_inputs(inp, device="cuda", hidden: bool = True) -> dict:
+    """All inputs of one workload as device tensors: ids/remap copied from the
+    host generator, real arrays filled on the device from their streams."""
+    import numpy as np
+    import torch
+
+    w = inp.w
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def gen(name, shape):
+        t = torch.empty(shape, dtype=dt, device=device)
+        stream_id, sigma, bias = inp.recipe(name)
+        fill(t, w.seed, stream_id, sigma, bias)
+        return t
+
+    out = {
+        "ids": torch.from_numpy(np.ascontiguousarray(inp.ids)).to(device),
+        "remap": torch.from_numpy(inp.remap).to(device),
+        "tables": gen("table", inp.table_shape()),
+        "w_kv": gen("wkv", inp.wkv_shape()),
+        "gamma_k": gen("gamma_k", (w.hc_mult, w.hidden)),
+        "gamma_q": gen("gamma_q", (w.hc_mult, w.hidden)),
+        "conv_w": gen("conv_w", (w.hc_mult, w.hidden, w.conv_kernel)),
+    }
+    if hidden:
+        out["hidden"] = gen("hidden", inp.hidden_shape())
+    return out
+
+
+def storage_numpy(t):
+    """A device tensor in the host generator's storage form (float32, or uint16 bf16 bits)."""
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()

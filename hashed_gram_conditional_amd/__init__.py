@@ -1,0 +1,299 @@
+"""Engram conditional-memory forward pass on MI355X: Python binding of libengram.so.
+
+Thin ctypes marshalling over the C ABI in include/engram.h.  Every step of the
+forward pass runs in the library's HIP kernels; torch is used only to own
+device memory and to name the stream.  The module raises ImportError if the
+library is not built, and there is no fallback.
+
+    cfg = EngramConfig.make(batch=4, seqlen=1024, ...)
+    p = Params(remap=..., tables=..., w_kv=..., gamma_k=..., gamma_q=..., conv_w=...)
+    out = forward(cfg, p, ids, hidden)            # [B][T][hc][d]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+from ._build import LIB_PATH, build  # noqa: F401
+
+MAX_ORDERS = 8
+MAX_HEADS = 64
+F32, BF16 = 0, 1
+
+STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too small",
+          -3: "HIP launch or API call failed", -4: "configuration not supported by the kernels"}
+
+# every entry point the header declares, in its order
+ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_gather",
+                "engram_project", "engram_gate_conv", "engram_forward", "engram_forward_timed",
+                "engram_forward_kernel_name", "engram_status_string"]
+
+
+class EngramError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class EngramConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("vocab", ctypes.c_int32),
+        ("n_orders", ctypes.c_int32), ("orders", ctypes.c_int32 * MAX_ORDERS),
+        ("heads_per_order", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("hidden", ctypes.c_int32), ("hc_mult", ctypes.c_int32),
+        ("conv_kernel", ctypes.c_int32), ("conv_dilation", ctypes.c_int32),
+        ("pad_id", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float), ("gate_clamp", ctypes.c_float),
+        ("multipliers", ctypes.c_int64 * MAX_ORDERS),
+        ("primes", ctypes.c_int64 * MAX_HEADS),
+    ]
+
+    @classmethod
+    def make(cls, *, batch: int, seqlen: int, vocab: int, orders: Sequence[int], heads_per_order: int,
+             head_dim: int, hidden: int, hc_mult: int, multipliers: Sequence[int], primes: Sequence[int],
+             conv_kernel: int = 4, conv_dilation: Optional[int] = None, pad_id: int = 0, dtype: str = "bf16",
+             norm_eps: float = 1e-6, gate_clamp: float = 1e-6) -> "EngramConfig":
+        c = cls()
+        c.batch, c.seqlen, c.vocab = batch, seqlen, vocab
+        if not 1 <= len(orders) <= MAX_ORDERS or len(primes) > MAX_HEADS or len(multipliers) > MAX_ORDERS:
+            raise ValueError("too many orders, heads or multipliers")
+        c.n_orders = len(orders)
+        for i, o in enumerate(orders):
+            c.orders[i] = int(o)
+        c.heads_per_order, c.head_dim, c.hidden, c.hc_mult = heads_per_order, head_dim, hidden, hc_mult
+        c.conv_kernel = conv_kernel
+        c.conv_dilation = max(orders) if conv_dilation is None else conv_dilation
+        c.pad_id = pad_id
+        c.dtype = BF16 if dtype == "bf16" else F32
+        c.norm_eps, c.gate_clamp = norm_eps, gate_clamp
+        for i, m in enumerate(multipliers):
+            c.multipliers[i] = int(m)
+        for i, p in enumerate(primes):
+            c.primes[i] = int(p)
+        return c
+
+    def with_shape(self, batch: int, seqlen: int) -> "EngramConfig":
+        c = EngramConfig.from_buffer_copy(self)
+        c.batch, c.seqlen = batch, seqlen
+        return c
+
+    @property
+    def n_heads(self) -> int:
+        return self.n_orders * self.heads_per_order
+
+    @property
+    def emb_dim(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def max_order(self) -> int:
+        return self.orders[self.n_orders - 1]
+
+    @property
+    def ring_len(self) -> int:
+        return (self.conv_kernel - 1) * self.conv_dilation
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("remap", ctypes.c_void_p), ("tables", ctypes.c_void_p), ("w_kv", ctypes.c_void_p),
+                ("gamma_k", ctypes.c_void_p), ("gamma_q", ctypes.c_void_p), ("conv_w", ctypes.c_void_p)]
+
+
+class _State(ctypes.Structure):
+    _fields_ = [("tok_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("g_ring", ctypes.c_void_p),
+                ("n_past", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """The loaded library; ImportError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        cfgp = ctypes.POINTER(EngramConfig)
+        prmp = ctypes.POINTER(_Params)
+        stp = ctypes.POINTER(_State)
+        lib.engram_workspace_size.argtypes = [cfgp]
+        lib.engram_workspace_size.restype = ctypes.c_size_t
+        lib.engram_state_bytes_per_sequence.argtypes = [cfgp]
+        lib.engram_state_bytes_per_sequence.restype = ctypes.c_size_t
+        lib.engram_hash.argtypes = [cfgp, prmp, P, stp, P, P]
+        lib.engram_gather.argtypes = [cfgp, prmp, P, P, P]
+        lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
+        lib.engram_gate_conv.argtypes = [cfgp, prmp, P, P, stp, P, P, P]
+        lib.engram_forward.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P]
+        lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int32)]
+        lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32]
+        lib.engram_forward_kernel_name.restype = ctypes.c_char_p
+        lib.engram_status_string.argtypes = [I]
+        lib.engram_status_string.restype = ctypes.c_char_p
+        for f in ("engram_hash", "engram_gather", "engram_project", "engram_gate_conv", "engram_forward",
+                  "engram_forward_timed"):
+            getattr(lib, f).restype = I
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("engram arguments must be device tensors")
+    if not t.is_contiguous():
+        raise ValueError("engram arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise EngramError(fn, rc)
+
+
+class Params:
+    """Device tensors of one Engram layer (see engram_params in include/engram.h)."""
+
+    def __init__(self, *, tables, w_kv, gamma_k, gamma_q, conv_w, remap=None):
+        self.remap, self.tables, self.w_kv = remap, tables, w_kv
+        self.gamma_k, self.gamma_q, self.conv_w = gamma_k, gamma_q, conv_w
+        self._c = _Params(_ptr(remap), _ptr(tables), _ptr(w_kv), _ptr(gamma_k), _ptr(gamma_q), _ptr(conv_w))
+
+
+class State:
+    """Decode state of `batch` sequences: token, value and gate rings plus n_past."""
+
+    def __init__(self, cfg: EngramConfig, batch: int, device="cuda"):
+        import torch
+
+        dt = torch.bfloat16 if cfg.dtype == BF16 else torch.float32
+        R = cfg.ring_len
+        self.tok_ring = torch.zeros((batch, max(cfg.max_order - 1, 1)), dtype=torch.int32, device=device)
+        self.v_ring = torch.zeros((batch, max(R, 1), cfg.hidden), dtype=dt, device=device)
+        self.g_ring = torch.zeros((batch, max(R, 1), cfg.hc_mult), dtype=torch.float32, device=device)
+        self.n_past = torch.zeros((batch,), dtype=torch.int64, device=device)
+        self._c = _State(_ptr(self.tok_ring), _ptr(self.v_ring), _ptr(self.g_ring), _ptr(self.n_past))
+
+    def clone(self) -> "State":
+        s = State.__new__(State)
+        s.tok_ring, s.v_ring = self.tok_ring.clone(), self.v_ring.clone()
+        s.g_ring, s.n_past = self.g_ring.clone(), self.n_past.clone()
+        s._c = _State(_ptr(s.tok_ring), _ptr(s.v_ring), _ptr(s.g_ring), _ptr(s.n_past))
+        return s
+
+
+def _real_dtype(cfg):
+    import torch
+
+    return torch.bfloat16 if cfg.dtype == BF16 else torch.float32
+
+
+def workspace_size(cfg: EngramConfig) -> int:
+    return load().engram_workspace_size(ctypes.byref(cfg))
+
+
+def state_bytes_per_sequence(cfg: EngramConfig) -> int:
+    return load().engram_state_bytes_per_sequence(ctypes.byref(cfg))
+
+
+def engram_hash(cfg: EngramConfig, p: Params, ids, state: Optional[State] = None, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.n_heads), dtype=torch.int32, device=ids.device)
+    st = None if state is None else ctypes.byref(state._c)
+    _check("engram_hash", load().engram_hash(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), st, _ptr(out),
+                                             _stream(stream)))
+    return out
+
+
+def engram_gather(cfg: EngramConfig, p: Params, idx, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.emb_dim), dtype=_real_dtype(cfg), device=idx.device)
+    _check("engram_gather", load().engram_gather(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(idx), _ptr(out),
+                                                 _stream(stream)))
+    return out
+
+
+def engram_project(cfg: EngramConfig, p: Params, e, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult + 1, cfg.hidden), dtype=_real_dtype(cfg),
+                          device=e.device)
+    _check("engram_project", load().engram_project(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(e), _ptr(out),
+                                                   _stream(stream)))
+    return out
+
+
+def engram_gate_conv(cfg: EngramConfig, p: Params, kv, hidden, state: Optional[State] = None, g_out=None, out=None,
+                     stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult, cfg.hidden), dtype=_real_dtype(cfg),
+                          device=kv.device)
+    if g_out is None:
+        g_out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult), dtype=torch.float32, device=kv.device)
+    st = None if state is None else ctypes.byref(state._c)
+    _check("engram_gate_conv", load().engram_gate_conv(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(kv),
+                                                       _ptr(hidden), st, _ptr(g_out), _ptr(out), _stream(stream)))
+    return out, g_out
+
+
+def alloc_workspace(cfg: EngramConfig, device="cuda"):
+    import torch
+
+    n = workspace_size(cfg)
+    if n == 0 and cfg.batch * cfg.seqlen > 0:
+        raise EngramError("engram_workspace_size", -1)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+def forward(cfg: EngramConfig, p: Params, ids, hidden, state: Optional[State] = None, out=None, workspace=None,
+            stream=None, events=None):
+    """Engram.forward: returns out [B][T][hc][d].  With `events` (a list of
+    2*k hipEvent_t handles) the i-th kernel is bracketed by events[2i], [2i+1]."""
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult, cfg.hidden), dtype=_real_dtype(cfg),
+                          device=ids.device)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, ids.device)
+    st = None if state is None else ctypes.byref(state._c)
+    lib = load()
+    if events is None:
+        rc = lib.engram_forward(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), st, _ptr(out),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+        _check("engram_forward", rc)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        nk = ctypes.c_int32(0)
+        rc = lib.engram_forward_timed(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), st, _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(stream), arr, len(events),
+                                      ctypes.byref(nk))
+        _check("engram_forward_timed", rc)
+    return out
+
+
+def kernel_names(cfg: EngramConfig, with_state: bool = False):
+    lib = load()
+    n = 5 if with_state else 4
+    return [lib.engram_forward_kernel_name(ctypes.byref(cfg), i).decode() for i in range(n)]

@@ -1,0 +1,357 @@
+// Host side of the Engram C ABI (include/engram.h): argument validation, the
+// per-call hash constants, the workspace layout of engram_forward and the
+// order of kernel launches.  Allocates nothing and keeps no mutable state.
+#include <math.h>
+#include <string.h>
+
+#include "engram_internal.h"
+
+using namespace engram;
+
+namespace {
+
+int max_order(const engram_config* c) { return c->orders[c->n_orders - 1]; }
+int n_heads(const engram_config* c) { return c->n_orders * c->heads_per_order; }
+int64_t emb_dim(const engram_config* c) { return (int64_t)n_heads(c) * c->head_dim; }
+int64_t esize(const engram_config* c) { return c->dtype == ENGRAM_BF16 ? 2 : 4; }
+int ring_len(const engram_config* c) { return (c->conv_kernel - 1) * c->conv_dilation; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+engram_status validate(const engram_config* c) {
+  if (c == nullptr) return ENGRAM_EINVAL;
+  if (c->batch < 0 || c->seqlen < 0 || c->vocab < 1) return ENGRAM_EINVAL;
+  if ((int64_t)c->batch * c->seqlen > INT32_MAX / 2) return ENGRAM_EUNSUPPORTED;
+  if (c->n_orders < 1 || c->n_orders > ENGRAM_MAX_ORDERS) return ENGRAM_EINVAL;
+  for (int i = 0; i < c->n_orders; i++) {
+    if (c->orders[i] < 1 || c->orders[i] > ENGRAM_MAX_ORDERS) return ENGRAM_EINVAL;
+    if (i > 0 && c->orders[i] <= c->orders[i - 1]) return ENGRAM_EINVAL;
+  }
+  if (c->heads_per_order < 1 || n_heads(c) > ENGRAM_MAX_HEADS) return ENGRAM_EINVAL;
+  for (int h = 0; h < n_heads(c); h++)
+    if (c->primes[h] < 1 || c->primes[h] > INT32_MAX) return ENGRAM_EINVAL;
+  if (c->dtype != ENGRAM_F32 && c->dtype != ENGRAM_BF16) return ENGRAM_EINVAL;
+  if (c->head_dim < 1 || c->hidden < 1 || c->hc_mult < 1 || c->hc_mult > ENGRAM_MAX_BRANCHES) return ENGRAM_EINVAL;
+  if (c->conv_kernel < 1 || c->conv_kernel > ENGRAM_MAX_CONV_KERNEL || c->conv_dilation < 1) return ENGRAM_EINVAL;
+  if (!(c->norm_eps >= 0.f) || !(c->gate_clamp >= 0.f)) return ENGRAM_EINVAL;
+  // 16-byte vectors along the hidden and embedding axes
+  if (c->hidden % 8 != 0 || emb_dim(c) % 8 != 0) return ENGRAM_EUNSUPPORTED;
+  if ((int64_t)(c->hc_mult + 1) * c->hidden > INT32_MAX / 4 || emb_dim(c) > INT32_MAX / 4) return ENGRAM_EUNSUPPORTED;
+  if ((int64_t)c->conv_kernel * c->conv_dilation > INT32_MAX / 4) return ENGRAM_EUNSUPPORTED;
+  return ENGRAM_OK;
+}
+
+engram_status check_params(const engram_config* c, const engram_params* p) {
+  if (p == nullptr || p->tables == nullptr || p->w_kv == nullptr || p->gamma_k == nullptr ||
+      p->gamma_q == nullptr || p->conv_w == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(p->tables, 16) || !aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) ||
+      !aligned(p->conv_w, 4))
+    return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+engram_status check_state(const engram_config* c, const engram_state* st) {
+  if (st == nullptr) return ENGRAM_OK;
+  if (st->n_past == nullptr) return ENGRAM_EINVAL;
+  if (max_order(c) > 1 && st->tok_ring == nullptr) return ENGRAM_EINVAL;
+  if (ring_len(c) > 0 && (st->v_ring == nullptr || st->g_ring == nullptr || !aligned(st->v_ring, 16)))
+    return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+void make_hash_consts(const engram_config* c, HashConsts* hc) {
+  memset(hc, 0, sizeof(*hc));
+  hc->n_orders = c->n_orders;
+  hc->heads_per_order = c->heads_per_order;
+  hc->n_heads = n_heads(c);
+  hc->max_order = max_order(c);
+  hc->pad_id = c->pad_id;
+  hc->vocab = c->vocab;
+  for (int i = 0; i < c->n_orders; i++) hc->orders[i] = c->orders[i];
+  for (int k = 0; k < ENGRAM_MAX_ORDERS; k++) hc->mult[k] = (uint64_t)c->multipliers[k];
+  int64_t off = 0;
+  for (int h = 0; h < n_heads(c); h++) {
+    const uint64_t p = (uint64_t)c->primes[h];
+    hc->prime[h] = (uint32_t)p;
+    hc->magic[h] = UINT64_MAX / p;
+    hc->wrap[h] = (uint32_t)((UINT64_MAX % p + 1) % p);
+    hc->row_off[h] = off;
+    off += (int64_t)p;
+  }
+}
+
+engram_status hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  void* e;
+  void* kv;
+  float* g;
+  size_t bytes;
+};
+
+Workspace carve(const engram_config* c, void* base) {
+  const int64_t N = (int64_t)c->batch * c->seqlen;
+  Workspace w;
+  size_t off = 0;
+  w.e = (uint8_t*)base + off;
+  off += align_up((size_t)N * emb_dim(c) * esize(c));
+  w.kv = (uint8_t*)base + off;
+  off += align_up((size_t)N * (c->hc_mult + 1) * c->hidden * esize(c));
+  w.g = (float*)((uint8_t*)base + off);
+  off += align_up((size_t)N * c->hc_mult * sizeof(float));
+  w.bytes = off;
+  return w;
+}
+
+const char* const kForwardKernels[] = {"hash_gather", "project_gemm", "gate", "short_conv", "advance_state"};
+
+GatherArgs gather_args(const engram_config* c, const engram_params* p, const int32_t* ids, const engram_state* st) {
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  a.ids = ids;
+  a.remap = p->remap;
+  a.tables = (const uint8_t*)p->tables;
+  a.tok_ring = st ? st->tok_ring : nullptr;
+  a.n_past = st ? st->n_past : nullptr;
+  a.batch = c->batch;
+  a.seqlen = c->seqlen;
+  a.row_bytes = (int32_t)(c->head_dim * esize(c));
+  return a;
+}
+
+GemmArgs gemm_args(const engram_config* c, const engram_params* p, const void* e, void* kv) {
+  GemmArgs g;
+  g.A = e;
+  g.B = p->w_kv;
+  g.C = kv;
+  g.M = c->batch * c->seqlen;
+  g.N = (c->hc_mult + 1) * c->hidden;
+  g.K = (int32_t)emb_dim(c);
+  return g;
+}
+
+GateArgs gate_args(const engram_config* c, const engram_params* p, const void* kv, const void* hidden, float* g) {
+  GateArgs a;
+  a.kv = kv;
+  a.hidden = hidden;
+  a.gamma_k = p->gamma_k;
+  a.gamma_q = p->gamma_q;
+  a.g_out = g;
+  a.n_tok = c->batch * c->seqlen;
+  a.hc = c->hc_mult;
+  a.d = c->hidden;
+  a.eps = c->norm_eps;
+  a.clamp = c->gate_clamp;
+  a.inv_sqrt_d = (float)(1.0 / sqrt((double)c->hidden));
+  a.bf16 = c->dtype == ENGRAM_BF16;
+  return a;
+}
+
+ConvArgs conv_args(const engram_config* c, const engram_params* p, const void* kv, const float* g, void* out,
+                   const engram_state* st) {
+  ConvArgs a;
+  a.v = (const uint8_t*)kv + (int64_t)c->hc_mult * c->hidden * esize(c);
+  a.v_stride = (int64_t)(c->hc_mult + 1) * c->hidden;
+  a.g = g;
+  a.conv_w = p->conv_w;
+  a.out = out;
+  a.v_ring = st ? st->v_ring : nullptr;
+  a.g_ring = st ? st->g_ring : nullptr;
+  a.n_past = st ? st->n_past : nullptr;
+  a.batch = c->batch;
+  a.seqlen = c->seqlen;
+  a.hc = c->hc_mult;
+  a.d = c->hidden;
+  a.ksize = c->conv_kernel;
+  a.dil = c->conv_dilation;
+  a.bf16 = c->dtype == ENGRAM_BF16;
+  return a;
+}
+
+// Records events[2i] before and events[2i+1] after launch i when asked to.
+struct Timer {
+  hipEvent_t* ev;
+  int n_ev;
+  int i = 0;
+  hipStream_t s;
+  hipError_t before() { return (ev && 2 * i + 1 < n_ev) ? hipEventRecord(ev[2 * i], s) : hipSuccess; }
+  hipError_t after() {
+    hipError_t e = (ev && 2 * i + 1 < n_ev) ? hipEventRecord(ev[2 * i + 1], s) : hipSuccess;
+    i++;
+    return e;
+  }
+};
+
+engram_status forward_impl(const engram_config* c, const engram_params* p, const int32_t* ids, const void* hidden,
+                           engram_state* st, void* out, void* ws, size_t ws_bytes, hipStream_t s, hipEvent_t* ev,
+                           int32_t n_ev, int32_t* n_kernels) {
+  engram_status rc = validate(c);
+  if (rc) return rc;
+  if ((rc = check_params(c, p)) || (rc = check_state(c, st))) return rc;
+  const int64_t N = (int64_t)c->batch * c->seqlen;
+  const int nk = st ? 5 : 4;
+  if (n_kernels) *n_kernels = N == 0 ? 0 : nk;
+  if (N == 0) return ENGRAM_OK;
+  if (ids == nullptr || hidden == nullptr || out == nullptr || ws == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(ws, 256)) return ENGRAM_EINVAL;
+  const Workspace w = carve(c, ws);
+  if (ws_bytes < w.bytes) return ENGRAM_ENOMEM;
+  const bool bf16 = c->dtype == ENGRAM_BF16;
+
+  HashConsts hc;
+  make_hash_consts(c, &hc);
+  Timer tm{ev, n_ev, 0, s};
+  hipError_t e;
+
+  GatherArgs ga = gather_args(c, p, ids, st);
+  ga.e_out = (uint8_t*)w.e;
+  if ((e = tm.before()) || (e = launch_hash_gather(hc, ga, true, s)) || (e = tm.after())) return hip_status(e);
+
+  const GemmArgs gm = gemm_args(c, p, w.e, w.kv);
+  if ((e = tm.before()) || (e = bf16 ? launch_gemm_bf16(gm, s) : launch_gemm_f32(gm, s)) || (e = tm.after()))
+    return hip_status(e);
+
+  const GateArgs gt = gate_args(c, p, w.kv, hidden, w.g);
+  if ((e = tm.before()) || (e = launch_gate(gt, s)) || (e = tm.after())) return hip_status(e);
+
+  const ConvArgs cv = conv_args(c, p, w.kv, w.g, out, st);
+  if ((e = tm.before()) || (e = launch_conv(cv, s)) || (e = tm.after())) return hip_status(e);
+
+  if (st) {
+    AdvanceArgs ad;
+    ad.ids = ids;
+    ad.remap = p->remap;
+    ad.vocab = c->vocab;
+    ad.pad_id = c->pad_id;
+    ad.v = cv.v;
+    ad.v_stride = cv.v_stride;
+    ad.g = w.g;
+    ad.tok_ring = st->tok_ring;
+    ad.v_ring = st->v_ring;
+    ad.g_ring = st->g_ring;
+    ad.n_past = st->n_past;
+    ad.batch = c->batch;
+    ad.seqlen = c->seqlen;
+    ad.hc = c->hc_mult;
+    ad.d = c->hidden;
+    ad.tok_ring_len = max_order(c) - 1;
+    ad.ring_len = ring_len(c);
+    ad.bf16 = bf16;
+    if ((e = tm.before()) || (e = launch_advance(ad, s)) || (e = tm.after())) return hip_status(e);
+  }
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t engram_workspace_size(const engram_config* cfg) {
+  if (validate(cfg)) return 0;
+  return carve(cfg, nullptr).bytes;
+}
+
+size_t engram_state_bytes_per_sequence(const engram_config* cfg) {
+  if (validate(cfg)) return 0;
+  const size_t R = (size_t)ring_len(cfg);
+  return (size_t)(max_order(cfg) - 1) * sizeof(int32_t) + R * cfg->hidden * esize(cfg) +
+         R * cfg->hc_mult * sizeof(float) + sizeof(int64_t);
+}
+
+engram_status engram_hash(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                          const engram_state* st, int32_t* idx_out, hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if (prm == nullptr) return ENGRAM_EINVAL;
+  if ((rc = check_state(cfg, st))) return rc;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (ids == nullptr || idx_out == nullptr) return ENGRAM_EINVAL;
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  a.ids = ids;
+  a.remap = prm->remap;
+  a.idx_out = idx_out;
+  a.tok_ring = st ? st->tok_ring : nullptr;
+  a.n_past = st ? st->n_past : nullptr;
+  a.batch = cfg->batch;
+  a.seqlen = cfg->seqlen;
+  a.row_bytes = (int32_t)(cfg->head_dim * esize(cfg));
+  return hip_status(launch_hash_gather(hc, a, true, stream));
+}
+
+engram_status engram_gather(const engram_config* cfg, const engram_params* prm, const int32_t* idx, void* e_out,
+                            hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if (prm == nullptr || prm->tables == nullptr || !aligned(prm->tables, 16)) return ENGRAM_EINVAL;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (idx == nullptr || e_out == nullptr || !aligned(e_out, 16)) return ENGRAM_EINVAL;
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  GatherArgs a = gather_args(cfg, prm, nullptr, nullptr);
+  a.idx_in = idx;
+  a.e_out = (uint8_t*)e_out;
+  return hip_status(launch_hash_gather(hc, a, false, stream));
+}
+
+engram_status engram_project(const engram_config* cfg, const engram_params* prm, const void* e, void* kv_out,
+                             hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if (prm == nullptr || prm->w_kv == nullptr || !aligned(prm->w_kv, 16)) return ENGRAM_EINVAL;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (e == nullptr || kv_out == nullptr || !aligned(e, 16) || !aligned(kv_out, 16)) return ENGRAM_EINVAL;
+  const GemmArgs g = gemm_args(cfg, prm, e, kv_out);
+  return hip_status(cfg->dtype == ENGRAM_BF16 ? launch_gemm_bf16(g, stream) : launch_gemm_f32(g, stream));
+}
+
+engram_status engram_gate_conv(const engram_config* cfg, const engram_params* prm, const void* kv, const void* hidden,
+                               const engram_state* st, float* g_out, void* out, hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if ((rc = check_params(cfg, prm)) || (rc = check_state(cfg, st))) return rc;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (kv == nullptr || hidden == nullptr || out == nullptr || g_out == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(kv, 16) || !aligned(hidden, 16) || !aligned(out, 16) || !aligned(g_out, 4)) return ENGRAM_EINVAL;
+  hipError_t e = launch_gate(gate_args(cfg, prm, kv, hidden, g_out), stream);
+  if (e) return hip_status(e);
+  return hip_status(launch_conv(conv_args(cfg, prm, kv, g_out, out, st), stream));
+}
+
+engram_status engram_forward(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                             const void* hidden, engram_state* st, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(cfg, prm, ids, hidden, st, out, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+engram_status engram_forward_timed(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                   const void* hidden, engram_state* st, void* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int32_t n_events,
+                                   int32_t* n_kernels) {
+  if (events == nullptr && n_events != 0) return ENGRAM_EINVAL;
+  return forward_impl(cfg, prm, ids, hidden, st, out, workspace, workspace_bytes, stream, events, n_events,
+                      n_kernels);
+}
+
+const char* engram_forward_kernel_name(const engram_config* cfg, int32_t i) {
+  if (validate(cfg) || i < 0 || i >= 5) return nullptr;
+  return kForwardKernels[i];
+}
+
+const char* engram_status_string(engram_status s) {
+  switch (s) {
+    case ENGRAM_OK: return "ok";
+    case ENGRAM_EINVAL: return "invalid configuration or argument";
+    case ENGRAM_ENOMEM: return "workspace too small";
+    case ENGRAM_EHIP: return "HIP launch or API call failed";
+    case ENGRAM_EUNSUPPORTED: return "configuration not supported by the kernels";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

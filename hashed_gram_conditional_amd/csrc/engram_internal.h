@@ -1,0 +1,122 @@
+// Internal declarations shared by the Engram HIP translation units: kernel
+// argument blocks, launchers and small device helpers.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/engram.h"
+
+namespace engram {
+
+// ----------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to nearest even; NaN stays NaN (quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool bf16) {
+  return bf16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// --------------------------------------------------------------- hashing
+// Everything the n-gram hash needs, passed by value (kernel arguments).
+struct HashConsts {
+  int32_t n_orders;
+  int32_t heads_per_order;
+  int32_t n_heads;
+  int32_t max_order;
+  int32_t pad_id;
+  int32_t vocab;
+  int32_t orders[ENGRAM_MAX_ORDERS];
+  uint64_t mult[ENGRAM_MAX_ORDERS];
+  uint32_t prime[ENGRAM_MAX_HEADS];
+  uint32_t wrap[ENGRAM_MAX_HEADS];    // 2^64 mod p: turns an unsigned residue into the int64 floored one
+  uint64_t magic[ENGRAM_MAX_HEADS];   // floor((2^64-1) / p) for Barrett reduction
+  int64_t row_off[ENGRAM_MAX_HEADS];  // first stacked-table row of each head
+};
+
+struct GatherArgs {
+  const int32_t* ids;       // [N] raw ids (hash mode)
+  const int32_t* remap;     // [vocab] or null
+  const int32_t* idx_in;    // [N][H] (gather-only mode)
+  int32_t* idx_out;         // [N][H] or null
+  const uint8_t* tables;    // stacked tables
+  uint8_t* e_out;           // [N][E] or null
+  const int32_t* tok_ring;  // [B][max_order-1] or null
+  const int64_t* n_past;    // [B] or null
+  int32_t batch, seqlen;
+  int32_t row_bytes;        // head_dim * element size
+};
+
+hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s);
+
+// ------------------------------------------------------------------ GEMM
+// C[M][N] = A[M][K] * B[N][K]^T (both operands K-contiguous), fp32 accumulate.
+struct GemmArgs {
+  const void* A;   // e   [M][K]
+  const void* B;   // w_kv [N][K]
+  void* C;         // kv  [M][N]
+  int32_t M, N, K;
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- gate / conv
+struct GateArgs {
+  const void* kv;        // [N][hc+1][d]
+  const void* hidden;    // [N][hc][d]
+  const void* gamma_k;   // [hc][d]
+  const void* gamma_q;   // [hc][d]
+  float* g_out;          // [N][hc]
+  int32_t n_tok, hc, d;
+  float eps, clamp, inv_sqrt_d;
+  bool bf16;
+};
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t s);
+
+struct ConvArgs {
+  const void* v;          // value rows, row stride v_stride elements
+  int64_t v_stride;
+  const float* g;         // [N][hc]
+  const void* conv_w;     // [hc][d][K]
+  void* out;              // [N][hc][d]
+  const void* v_ring;     // [B][R][d] or null
+  const float* g_ring;    // [B][R][hc] or null
+  const int64_t* n_past;  // [B] or null
+  int32_t batch, seqlen, hc, d, ksize, dil;
+  bool bf16;
+};
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
+
+struct AdvanceArgs {
+  const int32_t* ids;     // [B][T] raw
+  const int32_t* remap;   // or null
+  int32_t vocab, pad_id;
+  const void* v;          // value rows, stride v_stride
+  int64_t v_stride;
+  const float* g;         // [N][hc]
+  int32_t* tok_ring;
+  void* v_ring;
+  float* g_ring;
+  int64_t* n_past;
+  int32_t batch, seqlen, hc, d, tok_ring_len, ring_len;
+  bool bf16;
+};
+
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
+
+}  // namespace engram

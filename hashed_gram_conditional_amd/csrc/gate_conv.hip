@@ -1,0 +1,278 @@
+// K3: context-aware gate, value fusion, short causal conv and residual, plus
+// the decode-state update.
+//
+// Gate (formula sheet, kwkr.cn/news/37585, section 2.2 steps 1-2 and the full
+// formula in 2.3): per token and branch h, with K_h the key and Q_h the hidden
+// state of that branch,
+//   s = sum_c (K_c rk gk_c) (Q_c rq gq_c) / sqrt(d),  rk = (mean K^2 + eps)^-1/2
+//   g = sigmoid(sign(s) sqrt(max(|s|, clamp)))
+// One wavefront per (token, branch); each lane reads 16 bytes of K, Q and both
+// gammas per step and the three sums (K.K, Q.Q, K gk Q gq) are reduced across
+// the wavefront, so K and Q stream through once.
+//
+// Value fusion, conv and residual (formula sheet 2.2 step 3 and 3.2;
+// walk-through, yaoyuxiang.cn/news/830577, section 2.2-3: depthwise causal
+// conv, kernel 4, dilation = largest order):
+//   y_h[t] = Vg_h[t] + sum_j w_h[j] Vg_h[t - (K-1-j) D],  Vg_h = g_h V
+// A thread owns 8 channels of one branch and walks the positions
+// t0+r, t0+r+D, t0+r+2D, ... of one residue r mod D: every conv tap of the
+// next position is a position it has already visited, so the K-1 taps of
+// history stay in registers and each step loads one 16-byte slice of V, one
+// gate and writes one 16-byte slice of y.  The taps (8 channels x K) also stay
+// in registers for the whole walk.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+// 8 consecutive elements of a real array as floats
+__device__ __forceinline__ void load8(const void* p, int64_t i, bool bf16, float* v) {
+  if (bf16) {
+    const uint4 u = *(const uint4*)((const uint16_t*)p + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *(const float4*)((const float*)p + i);
+    const float4 b = *(const float4*)((const float*)p + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void store8(void* p, int64_t i, bool bf16, const float* v) {
+  if (bf16) {
+    uint4 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    *(uint4*)((uint16_t*)p + i) = u;
+  } else {
+    *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)((float*)p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+__device__ __forceinline__ float gate_activation(float s, float clamp) {
+  const float sgn = s > 0.f ? 1.f : (s < 0.f ? -1.f : 0.f);
+  const float a = sgn * sqrtf(fmaxf(fabsf(s), clamp));
+  return 1.f / (1.f + expf(-a));
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_gate(GateArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= (int64_t)a.n_tok * a.hc) return;
+  const int64_t n = wid / a.hc;
+  const int h = (int)(wid - n * a.hc);
+  const int64_t d = a.d;
+  const int64_t k_off = (n * (a.hc + 1) + h) * d;
+  const int64_t q_off = (n * a.hc + h) * d;
+  const int64_t g_off = (int64_t)h * d;
+  float kk = 0.f, qq = 0.f, kq = 0.f;
+  for (int64_t c = lane * 8; c < d; c += 512) {
+    float K[8], Q[8], gk[8], gq[8];
+    load8(a.kv, k_off + c, BF16, K);
+    load8(a.hidden, q_off + c, BF16, Q);
+    load8(a.gamma_k, g_off + c, BF16, gk);
+    load8(a.gamma_q, g_off + c, BF16, gq);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      kk = fmaf(K[i], K[i], kk);
+      qq = fmaf(Q[i], Q[i], qq);
+      kq = fmaf(K[i] * gk[i], Q[i] * gq[i], kq);
+    }
+  }
+  kk = wave_sum(kk);
+  qq = wave_sum(qq);
+  kq = wave_sum(kq);
+  if (lane == 0) {
+    const float inv_d = 1.f / (float)d;
+    const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
+    const float rq = 1.f / sqrtf(qq * inv_d + a.eps);
+    const float s = kq * rk * rq * a.inv_sqrt_d;
+    a.g_out[n * a.hc + h] = gate_activation(s, a.clamp);
+  }
+}
+
+constexpr int kConvIters = 16;  // positions a thread walks (stride D)
+
+template <bool BF16, int KS>
+__global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
+  const int groups = a.d >> 3;
+  const int gx = blockIdx.y * 256 + threadIdx.x;
+  if (gx >= a.hc * groups) return;
+  const int h = gx / groups;
+  const int c0 = (gx - h * groups) * 8;
+  const int D = a.dil;
+  const int T = a.seqlen;
+  const int run_len = D * kConvIters;
+  const int runs = (T + run_len - 1) / run_len;
+  int y = blockIdx.x;
+  const int r = y % D;
+  y /= D;
+  const int run = y % runs;
+  const int b = y / runs;
+  const int t_first = run * run_len + r;
+  if (t_first >= T) return;
+
+  const int64_t d = a.d;
+  const int R = (KS - 1) * D;
+  const int64_t past = a.n_past ? a.n_past[b] : 0;
+
+  float w[KS][8];  // taps of channel c0+i: conv_w[h][c0+i][0..KS)
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
+
+  // gated value at position t of this sequence (t may be negative: history)
+  auto vg_at = [&](int t, float* out) {
+    float g;
+    if (t >= 0) {
+      const int64_t n = (int64_t)b * T + t;
+      load8(a.v, n * a.v_stride + c0, BF16, out);
+      g = a.g[n * a.hc + h];
+    } else {
+      const int64_t p = past + t;
+      if (p < 0 || a.v_ring == nullptr) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) out[i] = 0.f;
+        return;
+      }
+      const int64_t slot = (int64_t)b * R + p % R;
+      load8(a.v_ring, slot * d + c0, BF16, out);
+      g = a.g_ring[slot * a.hc + h];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] *= g;
+  };
+
+  // hist[j] = Vg at t - (KS-1-j) D for j < KS-1
+  constexpr int NH = KS > 1 ? KS - 1 : 1;
+  float hist[NH][8];
+#pragma unroll
+  for (int j = 0; j < KS - 1; j++) vg_at(t_first - (KS - 1 - j) * D, hist[j]);
+
+  for (int it = 0; it < kConvIters; it++) {
+    const int t = t_first + it * D;
+    if (t >= T) break;
+    float cur[8], out[8];
+    vg_at(t, cur);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      float acc = fmaf(w[KS - 1][i], cur[i], cur[i]);
+#pragma unroll
+      for (int j = 0; j < KS - 1; j++) acc = fmaf(w[j][i], hist[j][i], acc);
+      out[i] = acc;
+    }
+    store8(a.out, (((int64_t)b * T + t) * a.hc + h) * d + c0, BF16, out);
+    if (KS > 1) {
+#pragma unroll
+      for (int j = 0; j + 1 < NH; j++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) hist[j][i] = hist[j + 1][i];
+#pragma unroll
+      for (int i = 0; i < 8; i++) hist[NH - 1][i] = cur[i];
+    }
+  }
+}
+
+// One workgroup per sequence: copy the newest positions of this call into the
+// rings, then advance n_past.  Runs after every kernel that reads the rings.
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_advance(AdvanceArgs a) {
+  const int b = blockIdx.x;
+  const int T = a.seqlen;
+  const int64_t past = a.n_past[b];
+  const int64_t d = a.d;
+  const int esz = BF16 ? 2 : 4;
+  // value and gate rings: last min(T, R) positions
+  if (a.ring_len > 0) {
+    const int cnt = T < a.ring_len ? T : a.ring_len;
+    const int t_lo = T - cnt;
+    const int64_t words = (int64_t)cnt * d * esz / 4;   // d % 8 == 0, so rows are whole 32-bit words
+    const int64_t row_words = d * esz / 4;
+    for (int64_t i = threadIdx.x; i < words; i += 256) {
+      const int tt = (int)(i / row_words);
+      const int64_t wd = i - tt * row_words;
+      const int t = t_lo + tt;
+      const int64_t slot = (int64_t)b * a.ring_len + (past + t) % a.ring_len;
+      const int64_t n = (int64_t)b * T + t;
+      const uint32_t* src = (const uint32_t*)((const uint8_t*)a.v + n * a.v_stride * esz);
+      ((uint32_t*)((uint8_t*)a.v_ring + slot * d * esz))[wd] = src[wd];
+    }
+    for (int i = threadIdx.x; i < cnt * a.hc; i += 256) {
+      const int tt = i / a.hc, h = i - tt * a.hc;
+      const int t = t_lo + tt;
+      const int64_t slot = (int64_t)b * a.ring_len + (past + t) % a.ring_len;
+      a.g_ring[slot * a.hc + h] = a.g[((int64_t)b * T + t) * a.hc + h];
+    }
+  }
+  if (a.tok_ring_len > 0) {
+    const int cnt = T < a.tok_ring_len ? T : a.tok_ring_len;
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+      const int t = T - cnt + i;
+      const int32_t id = a.ids[(int64_t)b * T + t];
+      int32_t x = a.pad_id;
+      if (id >= 0 && id < a.vocab) x = a.remap ? a.remap[id] : id;
+      a.tok_ring[(int64_t)b * a.tok_ring_len + (past + t) % a.tok_ring_len] = x;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.n_past[b] = past + T;
+}
+
+template <bool BF16>
+hipError_t conv_dispatch(const ConvArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.ksize) {
+    case 1: k_conv<BF16, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_conv<BF16, 2><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_conv<BF16, 3><<<grid, 256, 0, s>>>(a); break;
+    case 4: k_conv<BF16, 4><<<grid, 256, 0, s>>>(a); break;
+    case 5: k_conv<BF16, 5><<<grid, 256, 0, s>>>(a); break;
+    case 6: k_conv<BF16, 6><<<grid, 256, 0, s>>>(a); break;
+    case 7: k_conv<BF16, 7><<<grid, 256, 0, s>>>(a); break;
+    case 8: k_conv<BF16, 8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t s) {
+  const int64_t waves = (int64_t)a.n_tok * a.hc;
+  if (waves == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
+  if (a.bf16)
+    k_gate<true><<<blocks, 256, 0, s>>>(a);
+  else
+    k_gate<false><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
+  if ((int64_t)a.batch * a.seqlen == 0) return hipSuccess;
+  const int lanes = a.hc * (a.d / 8);
+  const int run_len = a.dil * kConvIters;
+  const int runs = (a.seqlen + run_len - 1) / run_len;
+  dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil), (lanes + 255) / 256);
+  return a.bf16 ? conv_dispatch<true>(a, grid, s) : conv_dispatch<false>(a, grid, s);
+}
+
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seqlen == 0) return hipSuccess;
+  if (a.bf16)
+    k_advance<true><<<a.batch, 256, 0, s>>>(a);
+  else
+    k_advance<false><<<a.batch, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -1,0 +1,140 @@
+// K1: compressed-token remap, time shifts, multi-head n-gram hash and the
+// gather of the hashed rows into e_t, fused in one kernel.
+//
+// Definitions: formula sheet (kwkr.cn/news/37585) section 1.2 steps 1-2 and
+// the full formula in 1.3 (mix = xor of t_k * m_k, hash = mix mod p_{n,j}),
+// section 4.2 (shift_k with pad_id); architecture walk-through
+// (yaoyuxiang.cn/news/830577) sections 2.2-1 and 4.3 (concatenate the rows of
+// all heads into e_t).
+//
+// Layout of the work: one 256-thread workgroup takes 16 consecutive tokens
+// (flattened over batch and time).  It stages the compressed ids of those
+// tokens plus the max_order-1 tokens before them in LDS (one remap lookup per
+// token instead of one per (token, head, offset)), hashes every (token, head)
+// pair into a global table row kept in LDS, then copies the rows to e_t in
+// 16-byte pieces: consecutive lanes take consecutive pieces of e_t, so a
+// 128-byte bf16 row is one 8-lane load and every store is coalesced, and each
+// lane keeps 8 independent row loads in flight before it stores.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokens = 16;
+constexpr int kUnroll = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte piece
+
+// Floored modulo of the int64 value with bit pattern u by p (numpy's `%` on
+// int64): Barrett reduction of the unsigned value with magic = floor((2^64-1)/p)
+// leaves a residue below 3p; if u is negative as int64 its value is u - 2^64,
+// whose residue is (u mod p) - (2^64 mod p), brought back into [0, p).
+__device__ __forceinline__ uint32_t floored_mod(uint64_t u, uint32_t p, uint64_t magic, uint32_t wrap) {
+  const uint64_t q = __umul64hi(u, magic);
+  uint64_t r = u - q * (uint64_t)p;
+  if (r >= p) r -= p;
+  if (r >= p) r -= p;
+  if ((int64_t)u < 0) {
+    r += (uint64_t)(p - wrap);
+    if (r >= p) r -= p;
+  }
+  return (uint32_t)r;
+}
+
+template <typename Chunk>
+__global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherArgs a, int compute_hash) {
+  __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
+  __shared__ int64_t s_row[kTokens * ENGRAM_MAX_HEADS];
+
+  const int64_t N = (int64_t)a.batch * a.seqlen;
+  const int64_t n0 = (int64_t)blockIdx.x * kTokens;
+  const int ntok = (int)min((int64_t)kTokens, N - n0);
+  const int H = hc.n_heads;
+  const int tid = threadIdx.x;
+
+  if (compute_hash) {
+    const int W = hc.max_order - 1;
+    for (int i = tid; i < ntok + W; i += kThreads) {
+      const int64_t n = n0 - W + i;
+      int32_t x = hc.pad_id;
+      if (n >= 0) {
+        const int32_t id = a.ids[n];
+        if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
+      }
+      s_x[i] = x;
+    }
+    __syncthreads();
+    for (int pr = tid; pr < ntok * H; pr += kThreads) {
+      const int ti = pr / H, h = pr - ti * H;
+      const int64_t n = n0 + ti;
+      const int64_t b = n / a.seqlen;
+      const int32_t t = (int32_t)(n - b * a.seqlen);
+      const int order = hc.orders[h / hc.heads_per_order];
+      uint64_t mix = 0;
+      for (int k = 0; k < order; k++) {
+        int32_t tok;
+        if (t - k >= 0) {
+          tok = s_x[W + ti - k];
+        } else {
+          const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
+          tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
+        }
+        mix ^= (uint64_t)(int64_t)tok * hc.mult[k];
+      }
+      const uint32_t r = floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
+      if (a.idx_out) a.idx_out[n * H + h] = (int32_t)r;
+      s_row[ti * H + h] = hc.row_off[h] + r;
+    }
+  } else {
+    for (int pr = tid; pr < ntok * H; pr += kThreads) {
+      const int ti = pr / H, h = pr - ti * H;
+      int32_t r = a.idx_in[(n0 + ti) * H + h];
+      r = r < 0 ? 0 : (r >= (int32_t)hc.prime[h] ? (int32_t)hc.prime[h] - 1 : r);
+      s_row[ti * H + h] = hc.row_off[h] + r;
+    }
+  }
+  __syncthreads();
+  if (a.e_out == nullptr) return;
+
+  const int cpr = a.row_bytes / (int)sizeof(Chunk);  // pieces per table row
+  const int cpt = H * cpr;                           // pieces per token
+  const int total = ntok * cpt;
+  const Chunk* __restrict__ tab = reinterpret_cast<const Chunk*>(a.tables);
+  Chunk* __restrict__ e = reinterpret_cast<Chunk*>(a.e_out) + n0 * cpt;
+  auto src = [&](int c) -> const Chunk* {
+    const int ti = c / cpt;
+    const int r = c - ti * cpt;
+    const int h = r / cpr;
+    const int col = r - h * cpr;
+    return tab + s_row[ti * H + h] * cpr + col;
+  };
+  int base = tid;
+  // full rounds: kUnroll independent row loads in flight per lane, then the stores
+  for (; base + (kUnroll - 1) * kThreads < total; base += kThreads * kUnroll) {
+    Chunk v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) v[u] = *src(base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) e[base + u * kThreads] = v[u];
+  }
+  for (int c = base; c < total; c += kThreads) e[c] = *src(c);
+}
+
+}  // namespace
+
+hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s) {
+  const int64_t N = (int64_t)a.batch * a.seqlen;
+  if (N == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((N + kTokens - 1) / kTokens);
+  const int ch = compute_hash ? 1 : 0;
+  if (a.row_bytes % 16 == 0)
+    k_hash_gather<u32x4><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+  else if (a.row_bytes % 4 == 0)
+    k_hash_gather<uint32_t><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+  else
+    k_hash_gather<uint16_t><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -1,0 +1,173 @@
+/*
+ * engram.h - C ABI of the Engram conditional-memory forward pass on MI355X (gfx950).
+ *
+ * The Engram module (architecture walk-through at yaoyuxiang.cn/news/830577,
+ * sections 2.2 and 4.2-4.3; formula sheet at kwkr.cn/news/37585, sections 1-5)
+ * looks up hashed n-grams of compressed token ids in multi-head embedding
+ * tables, gates the retrieved memory against the hidden state of each branch,
+ * and smooths it with a short causal depthwise conv plus a residual:
+ *
+ *   x        = remap[ids]                                    (compressed ids)
+ *   s_k[t]   = x[t-k], or pad_id before the sequence start    (time shift)
+ *   mix_n[t] = xor_{k<n} s_k[t] * m_k   (wrapping int64)
+ *   idx      = mix_n mod p_{n,j}        (floored, in [0, p))  per order n, head j
+ *   e[t]     = concat_{n,j} table_{n,j}[idx]                  (E = H * head_dim)
+ *   K_h      = W_k,h e,  V = W_v e                            (no bias)
+ *   s_h      = <RMSNorm(K_h) * gk_h, RMSNorm(Q_h) * gq_h> / sqrt(d), Q_h = hidden[t][h]
+ *   g_h      = sigmoid(sign(s_h) * sqrt(max(|s_h|, gate_clamp)))
+ *   Vg_h[t]  = g_h[t] * V[t]
+ *   out_h[t] = Vg_h[t] + sum_j w_h[j] * Vg_h[t - (conv_kernel-1-j) * dilation]
+ *
+ * Conventions for every call:
+ *  - Array arguments are DEVICE pointers, allocated and owned by the caller.
+ *    The library allocates no memory and keeps no mutable global state; calls
+ *    on different streams with disjoint outputs may run concurrently.
+ *  - Calls validate their arguments on the host, enqueue kernels on `stream`
+ *    (NULL = the null stream) and return without waiting.  A status other than
+ *    ENGRAM_OK means nothing was enqueued.  Faults inside kernels surface as HIP
+ *    errors at the caller's next synchronisation.
+ *  - Layouts are dense row-major with the last index fastest.  N = batch*seqlen.
+ *  - dtype selects the storage of tables, weights, gammas, conv taps, hidden,
+ *    out and the value history: float32, or bfloat16 with float32 accumulation.
+ *  - Token ids outside [0, vocab) are read as pad_id.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_MAX_ORDERS 8
+#define ENGRAM_MAX_HEADS 64
+#define ENGRAM_MAX_BRANCHES 16
+#define ENGRAM_MAX_CONV_KERNEL 8
+
+typedef enum {
+  ENGRAM_OK = 0,
+  ENGRAM_EINVAL = -1,       /* invalid configuration or argument */
+  ENGRAM_ENOMEM = -2,       /* workspace smaller than engram_workspace_size() */
+  ENGRAM_EHIP = -3,         /* a HIP launch or API call failed */
+  ENGRAM_EUNSUPPORTED = -4  /* valid configuration outside what the kernels handle */
+} engram_status;
+
+typedef enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 } engram_dtype;
+
+/* Hyper-parameters of one Engram layer and the shape of one call.
+ * Host memory, read during the call only. */
+typedef struct engram_config {
+  int32_t batch;            /* B sequences */
+  int32_t seqlen;           /* T new tokens per sequence (T = 1 for a decode step) */
+  int32_t vocab;            /* raw vocabulary size V; remap has V entries */
+  int32_t n_orders;         /* number of n-gram orders, 1..ENGRAM_MAX_ORDERS */
+  int32_t orders[ENGRAM_MAX_ORDERS];   /* ascending n-gram orders, each >= 1 */
+  int32_t heads_per_order;  /* hash heads per order; H = n_orders * heads_per_order <= ENGRAM_MAX_HEADS */
+  int32_t head_dim;         /* embedding width of one head; E = H * head_dim, E % 8 == 0 */
+  int32_t hidden;           /* d, hidden size of one branch; d % 8 == 0 */
+  int32_t hc_mult;          /* branches (hyper-connection channels), 1..ENGRAM_MAX_BRANCHES */
+  int32_t conv_kernel;      /* short-conv taps, 1..ENGRAM_MAX_CONV_KERNEL (4 on the pages) */
+  int32_t conv_dilation;    /* >= 1 (the largest order on the pages) */
+  int32_t pad_id;           /* compressed id hashed for positions before the sequence start */
+  int32_t dtype;            /* engram_dtype */
+  float norm_eps;           /* RMSNorm epsilon, >= 0 */
+  float gate_clamp;         /* lower clamp of |s| before the square root (1e-6 on the pages), >= 0 */
+  int64_t multipliers[ENGRAM_MAX_ORDERS]; /* m_k for k < largest order: m_k multiplies the token k back */
+  int64_t primes[ENGRAM_MAX_HEADS];       /* modulus (table rows) of each head, order-major, 1..2^31-1 */
+} engram_config;
+
+/* Layer parameters (device pointers, read only). Head h's table occupies rows
+ * [sum_{h'<h} primes[h'], + primes[h]) of one stacked table. */
+typedef struct engram_params {
+  const int32_t *remap;     /* [vocab] raw -> compressed id; NULL: ids are already compressed */
+  const void *tables;       /* [sum primes][head_dim] dtype */
+  const void *w_kv;         /* [(hc_mult+1)*hidden][E] dtype: key rows of branch 0..hc-1, then value rows */
+  const void *gamma_k;      /* [hc_mult][hidden] dtype, RMSNorm scale of the keys */
+  const void *gamma_q;      /* [hc_mult][hidden] dtype, RMSNorm scale of the queries (hidden states) */
+  const void *conv_w;       /* [hc_mult][hidden][conv_kernel] dtype; tap conv_kernel-1 is the current position */
+} engram_params;
+
+/* Per-sequence decode state (device arrays owned by the caller). Rings hold the
+ * most recent positions: absolute position p lives in slot p % ring length.
+ * n_past[b] counts the tokens sequence b has consumed; 0 means a fresh
+ * sequence, whose rings need no initialisation. */
+typedef struct engram_state {
+  int32_t *tok_ring;        /* [B][max_order-1] compressed ids (unused when max_order == 1) */
+  void *v_ring;             /* [B][(conv_kernel-1)*conv_dilation][hidden] dtype, value projections */
+  float *g_ring;            /* [B][(conv_kernel-1)*conv_dilation][hc_mult] gates */
+  int64_t *n_past;          /* [B] */
+} engram_state;
+
+/* Bytes of workspace engram_forward needs for this configuration (0 when
+ * the configuration is invalid). */
+size_t engram_workspace_size(const engram_config *cfg);
+
+/* Bytes of decode state per sequence, summed over the three rings (0 when invalid). */
+size_t engram_state_bytes_per_sequence(const engram_config *cfg);
+
+/* N-gram hash indices (formula sheet 1.2-1.3, time shift 4.2; walk-through 4.2).
+ * ids: [B][T] raw token ids.  st: NULL for fresh sequences (pad history), or a
+ * state whose token ring and n_past supply the tokens before position 0; it is
+ * read, not advanced.  idx_out: [B][T][H] int32, the row within head h's table. */
+engram_status engram_hash(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                          const engram_state *st, int32_t *idx_out, hipStream_t stream);
+
+/* Multi-head embedding lookup and concatenation into e_t (walk-through 2.2-1
+ * and 4.3).  idx: [B][T][H] as written by engram_hash; entries outside
+ * [0, primes[h]) are clamped into range.  e_out: [B][T][E] dtype, exact copies
+ * of the table rows. */
+engram_status engram_gather(const engram_config *cfg, const engram_params *prm, const int32_t *idx,
+                            void *e_out, hipStream_t stream);
+
+/* Key and value projections (formula sheet 2.2 steps 1 and 3): kv_out[n] =
+ * w_kv . e[n], i.e. [B][T][hc_mult+1][hidden] dtype with the keys of each
+ * branch first and the shared value last.  bf16 uses MFMA with float32
+ * accumulation and one rounding at the store. */
+engram_status engram_project(const engram_config *cfg, const engram_params *prm, const void *e,
+                             void *kv_out, hipStream_t stream);
+
+/* Gate, value fusion, short conv and residual (formula sheet 2.2-2.3 and 3.2;
+ * walk-through 2.2-3).  kv: [B][T][hc_mult+1][hidden] dtype from
+ * engram_project; hidden: [B][T][hc_mult][hidden] dtype; st: NULL (zero
+ * history) or a state whose rings supply V and g before position 0, read and
+ * not advanced.  g_out: [B][T][hc_mult] float32, receives the gates (required:
+ * the conv reads them back); out: [B][T][hc_mult][hidden] dtype. */
+engram_status engram_gate_conv(const engram_config *cfg, const engram_params *prm, const void *kv,
+                               const void *hidden, const engram_state *st, float *g_out, void *out,
+                               hipStream_t stream);
+
+/* The whole module (walk-through 4.3, Engram.forward): ids [B][T] raw ids,
+ * hidden [B][T][hc_mult][hidden] -> out [B][T][hc_mult][hidden].  workspace:
+ * device memory of at least engram_workspace_size(cfg) bytes (ENGRAM_ENOMEM if
+ * shorter).  st: NULL, or a state that the call continues and then advances
+ * (rings updated, n_past += T), so a prefill followed by decode steps gives the
+ * outputs of one prefill over the whole sequence. */
+engram_status engram_forward(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                             const void *hidden, engram_state *st, void *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Same as engram_forward, additionally recording events[2i] / events[2i+1]
+ * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,
+ * for i < n_events/2.  Returns the number of kernels in *n_kernels (nullable).
+ * Names of those kernels: engram_forward_kernel_name(cfg, i). */
+engram_status engram_forward_timed(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                   const void *hidden, engram_state *st, void *out, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                                   int32_t n_events, int32_t *n_kernels);
+
+/* Static name of the i-th kernel engram_forward launches for cfg (NULL past the end). */
+const char *engram_forward_kernel_name(const engram_config *cfg, int32_t i);
+
+/* Static description of a status code. */
+const char *engram_status_string(engram_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -1,0 +1,116 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry point
+include/engram.h declares, and validates configurations before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+
+
+@pytest.fixture(scope="module")
+def eg():
+    import hashed_gram_conditional_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        m.build()
+    m.load()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(engram_[a-z_]+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_four_pages_calls():
+    names = declared_functions()
+    for n in ("engram_hash", "engram_gather", "engram_gate_conv", "engram_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(eg):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    out = subprocess.run(["nm", "-D", "--defined-only", eg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(names) == sorted(eg.ENTRY_POINTS)
+    lib = ctypes.CDLL(eg.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def good(eg, **over):
+    kw = dict(batch=2, seqlen=16, vocab=100, orders=[2, 3], heads_per_order=2, head_dim=16, hidden=32, hc_mult=2,
+              multipliers=[3, 5, 7], primes=[11, 13, 17, 19], dtype="bf16")
+    kw.update(over)
+    return eg.EngramConfig.make(**kw)
+
+
+def test_workspace_and_state_sizes(eg):
+    c = good(eg)
+    N, E, d, hc = 32, 64, 32, 2
+    ws = eg.workspace_size(c)
+    assert ws >= N * E * 2 + N * (hc + 1) * d * 2 + N * hc * 4
+    assert ws % 256 == 0
+    R = 3 * 3
+    assert eg.state_bytes_per_sequence(c) == 2 * 4 + R * d * 2 + R * hc * 4 + 8
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(orders=[3, 2]), -1), (dict(orders=[0, 3]), -1), (dict(heads_per_order=0), -1),
+    (dict(hidden=36), -4), (dict(head_dim=3, heads_per_order=1, primes=[11, 13]), -4),
+    (dict(hc_mult=0), -1), (dict(hc_mult=17), -1), (dict(conv_kernel=9), -1), (dict(conv_dilation=0), -1),
+    (dict(primes=[11, 0, 17, 19]), -1), (dict(primes=[11, 13, 17, 2**31]), -1), (dict(vocab=0), -1),
+    (dict(batch=-1), -1), (dict(norm_eps=-1.0), -1),
+])
+def test_invalid_configs_are_rejected_on_the_host(eg, over, status):
+    c = good(eg, **over)
+    assert eg.workspace_size(c) == 0
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    # validation fails before any pointer is touched or kernel enqueued
+    rc = lib.engram_hash(ctypes.byref(c), ctypes.byref(prm), P(16), None, P(16), None)
+    assert rc == status
+    rc = lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), P(16), P(16), None, P(16), P(256), 1 << 30, None)
+    assert rc == status
+
+
+def test_forward_rejects_short_workspace_and_null_pointers(eg):
+    c = good(eg)
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    ws = eg.workspace_size(c)
+    assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), P(16), P(16), None, P(16), P(256), ws - 1,
+                              None) == -2
+    assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), None, P(16), None, P(16), P(256), ws, None) == -1
+    prm_bad = eg._Params(P(16), None, P(16), P(16), P(16), P(16))
+    assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm_bad), P(16), P(16), None, P(16), P(256), ws,
+                              None) == -1
+    # misaligned device pointers
+    assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), P(16), P(18), None, P(16), P(256), ws, None) == -1
+
+
+def test_empty_calls_succeed_without_launching(eg):
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    for B, T in ((0, 16), (2, 0)):
+        c = good(eg, batch=B, seqlen=T)
+        assert lib.engram_hash(ctypes.byref(c), ctypes.byref(prm), None, None, None, None) == 0
+        assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), None, None, None, None, None, 0, None) == 0
+
+
+def test_status_strings_and_kernel_names(eg):
+    lib = eg.load()
+    assert lib.engram_status_string(-2) == b"workspace too small"
+    assert eg.kernel_names(good(eg), with_state=True) == ["hash_gather", "project_gemm", "gate", "short_conv",
+                                                         "advance_state"]

@@ -1,0 +1,298 @@
+"""GPU parity: every C-ABI call against the oracle on the seeded workloads.
+
+Bars: hash indices and gathered rows bit-exact; outputs within max|y - y_ref| /
+max|y_ref| <= 1e-5 on the float32 workload and <= 2e-2 on the bf16 ones.
+"""
+import numpy as np
+import pytest
+
+from cases import TOL, Case, normwise, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def eg():
+    import hashed_gram_conditional_amd as m
+
+    m.load()
+    return m
+
+
+_cases = {}
+
+
+def case(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _cases:
+        _cases[key] = Case(name, **over)
+    return _cases[key]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ inputs
+@pytest.mark.parametrize("name", ["tiny_fp32", "b4_t1024"])
+def test_device_fill_matches_host_generator(eg, name):
+    from engram_synth.device import storage_numpy
+
+    c = case(name)
+    d = c.dev
+    rng = np.random.default_rng(0)
+    rows = rng.choice(c.w.table_rows, size=64, replace=False)
+    assert np.array_equal(storage_numpy(d["tables"])[rows], c.inp.table_rows(rows))
+    assert np.array_equal(storage_numpy(d["w_kv"]), c.wkv)
+    gk, gq, cw = c.small
+    assert np.array_equal(storage_numpy(d["gamma_k"]), gk)
+    assert np.array_equal(storage_numpy(d["conv_w"]), cw)
+    hb = rng.integers(0, c.B, 8)
+    ht = rng.integers(0, c.T, 8)
+    assert np.array_equal(storage_numpy(d["hidden"])[hb, ht], c.inp.hidden_at(hb, ht))
+
+
+# ------------------------------------------------------------------ hash
+@pytest.mark.parametrize("name", ["tiny_fp32", "b4_t1024", "b8_t4096"])
+def test_hash_bit_exact(eg, name):
+    c = case(name)
+    idx = eg.engram_hash(c.cfg(), c.params, c.dev["ids"])
+    sync()
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), c.idx)
+
+
+def test_hash_edge_cases(eg):
+    c = case("tiny_fp32")
+    p = c.params
+    ids = c.dev["ids"]
+    # ragged lengths, T shorter than the largest order, a single token
+    for T in (1, 2, 3, 17, 63):
+        got = eg.engram_hash(c.cfg(1, T), p, ids[:, :T].contiguous())
+        sync()
+        assert np.array_equal(got.cpu().numpy(), c.orc.with_shape(1, T).hash(c.inp.ids[:, :T], remap=c.inp.remap))
+    # empty calls enqueue nothing and succeed
+    eg.engram_hash(c.cfg(0, 64), p, ids)
+    eg.engram_hash(c.cfg(1, 0), p, ids)
+    # out-of-range raw ids hash as pad_id
+    bad = c.inp.ids.copy()
+    bad[0, [5, 40]] = [-3, c.w.vocab + 7]
+    got = eg.engram_hash(c.cfg(), p, torch.from_numpy(bad).cuda())
+    sync()
+    x = c.inp.remap[np.clip(bad, 0, c.w.vocab - 1)]
+    x[0, [5, 40]] = c.w.pad_id
+    assert np.array_equal(got.cpu().numpy(), c.orc.hash(x))
+
+
+def test_hash_negative_multipliers_and_pad(eg):
+    """Multipliers across the whole int64 range (negative mixes) and a nonzero pad."""
+    import hashed_gram_conditional_amd as m
+    import oracle as orc
+
+    rng = np.random.default_rng(5)
+    mults = [int(v) for v in rng.integers(-(2**63), 2**63 - 1, size=4, dtype=np.int64)]
+    primes = [2, 3, 1009, 65537, 2147483647, 999983]
+    kw = dict(batch=3, seqlen=45, orders=[1, 2, 4], heads_per_order=2, head_dim=8, hidden=8, hc_mult=1,
+              multipliers=mults, primes=primes, pad_id=123456)
+    cfg = m.EngramConfig.make(vocab=1 << 30, dtype="f32", **kw)
+    o = orc.Oracle(dtype="f32", **kw)
+    ids = rng.integers(0, 1 << 30, size=(3, 45)).astype(np.int32)
+    tables = torch.zeros((8, 8), device="cuda")
+    p = m.Params(tables=tables, w_kv=tables, gamma_k=tables, gamma_q=tables, conv_w=tables)
+    got = m.engram_hash(cfg, p, torch.from_numpy(ids).cuda())
+    sync()
+    assert np.array_equal(got.cpu().numpy(), o.hash(ids))
+
+
+# ------------------------------------------------------------------ gather
+@pytest.mark.parametrize("name", ["tiny_fp32", "b4_t1024", "b8_t4096"])
+def test_gather_bit_exact(eg, name):
+    from engram_synth.device import storage_numpy
+
+    c = case(name)
+    idx = eg.engram_hash(c.cfg(), c.params, c.dev["ids"])
+    e = eg.engram_gather(c.cfg(), c.params, idx)
+    sync()
+    N = c.B * c.T
+    pos = np.arange(N) if N <= 4096 else c.sample_positions(2048, seed=1)
+    got = storage_numpy(e).reshape(N, -1)[pos]
+    assert np.array_equal(got, c.e_at(pos))
+
+
+# ------------------------------------------------------------------ projections
+@pytest.mark.parametrize("name", ["tiny_fp32", "b4_t1024"])
+def test_project_within_tolerance(eg, name):
+    c = case(name)
+    idx = eg.engram_hash(c.cfg(), c.params, c.dev["ids"])
+    e = eg.engram_gather(c.cfg(), c.params, idx)
+    kv = eg.engram_project(c.cfg(), c.params, e)
+    sync()
+    from engram_synth.device import storage_numpy
+
+    N = c.B * c.T
+    pos = np.arange(N) if N <= 64 else c.sample_positions(128, seed=2)
+    e_np = storage_numpy(e).reshape(N, -1)[pos]
+    ref = c.orc.project(c.wkv, e_np)
+    err = normwise(to_f64(kv).reshape(N, -1)[pos], ref.reshape(len(pos), -1))
+    # bf16: one rounding of a float32-accumulated dot product (relative 2^-9) bounds it
+    assert err <= (1e-6 if c.w.dtype == "f32" else 4e-3), err
+
+
+@pytest.mark.parametrize("shape", [(3, 77, 2, 3, 8, 40, 2), (1, 300, 3, 1, 16, 24, 3), (2, 129, 2, 4, 16, 136, 1)])
+def test_project_ragged_tiles(eg, shape):
+    """Token, channel and reduction counts that are not multiples of the GEMM tiles."""
+    import hashed_gram_conditional_amd as m
+    import oracle as orc
+
+    B, T, n_orders, K, Dh, d, hc = shape
+    orders = list(range(2, 2 + n_orders))
+    H = n_orders * K
+    E = H * Dh
+    rng = np.random.default_rng(sum(shape))
+    kw = dict(batch=B, seqlen=T, orders=orders, heads_per_order=K, head_dim=Dh, hidden=d, hc_mult=hc,
+              multipliers=[3, 5, 7, 9, 11], primes=[101 + 2 * i for i in range(H)])
+    for dtype in ("f32", "bf16"):
+        cfg = m.EngramConfig.make(vocab=1000, dtype=dtype, **kw)
+        o = orc.Oracle(dtype=dtype, **kw)
+        w = rng.standard_normal(((hc + 1) * d, E)).astype(np.float32)
+        e = rng.standard_normal((B * T, E)).astype(np.float32)
+        if dtype == "bf16":
+            wt = torch.from_numpy(w).to(torch.bfloat16)
+            et = torch.from_numpy(e).to(torch.bfloat16)
+        else:
+            wt, et = torch.from_numpy(w), torch.from_numpy(e)
+        from engram_synth.device import storage_numpy
+
+        ref = o.project(storage_numpy(wt), storage_numpy(et)).reshape(B * T, -1)
+        wt, et = wt.cuda(), et.cuda()
+        p = m.Params(tables=wt, w_kv=wt, gamma_k=wt, gamma_q=wt, conv_w=wt)
+        kv = m.engram_project(cfg, p, et)
+        sync()
+        err = normwise(to_f64(kv).reshape(B * T, -1), ref)
+        assert err <= (1e-6 if dtype == "f32" else 4e-3), (dtype, err)
+
+
+# ------------------------------------------------------------------ gate + conv
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("strong", [False, True])
+def test_gate_conv_with_oracle_kv(eg, dtype, strong):
+    """Gate, conv and residual alone, fed the oracle's projections; strong conv
+    taps and spread gammas make a dropped or shifted tap show."""
+    import hashed_gram_conditional_amd as m
+    import oracle as orc
+    from engram_synth.device import storage_numpy
+
+    B, T, d, hc, D = 2, 70, 48, 3, 3
+    rng = np.random.default_rng(7 + strong)
+    kw = dict(batch=B, seqlen=T, orders=[2, 3], heads_per_order=1, head_dim=8, hidden=d, hc_mult=hc,
+              multipliers=[3, 5, 7], primes=[11, 13])
+    cfg = m.EngramConfig.make(vocab=10, dtype=dtype, **kw)
+    o = orc.Oracle(dtype=dtype, **kw)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kv = torch.from_numpy(rng.standard_normal((B, T, hc + 1, d)).astype(np.float32) * 0.02).to(tdt)
+    hid = torch.from_numpy(rng.standard_normal((B, T, hc, d)).astype(np.float32)).to(tdt)
+    sc = 0.5 if strong else 0.02
+    cw = torch.from_numpy(rng.standard_normal((hc, d, 4)).astype(np.float32) * sc).to(tdt)
+    lo, hi = (0.5, 1.5) if strong else (0.98, 1.02)
+    gk = torch.from_numpy(rng.uniform(lo, hi, (hc, d)).astype(np.float32)).to(tdt)
+    gq = torch.from_numpy(rng.uniform(lo, hi, (hc, d)).astype(np.float32)).to(tdt)
+    kv_ref = (kv.to(torch.float64).numpy()).reshape(B * T, hc + 1, d)
+    g_ref = o.gate(storage_numpy(gk), storage_numpy(gq), kv_ref, storage_numpy(hid).reshape(B * T, hc, d))
+    y_ref = o.conv(storage_numpy(cw), kv_ref, g_ref)
+    dv = {k: v.cuda() for k, v in dict(kv=kv, hid=hid, cw=cw, gk=gk, gq=gq).items()}
+    p = m.Params(tables=dv["kv"], w_kv=dv["kv"], gamma_k=dv["gk"], gamma_q=dv["gq"], conv_w=dv["cw"])
+    y, g = m.engram_gate_conv(cfg, p, dv["kv"], dv["hid"])
+    sync()
+    assert normwise(to_f64(g).reshape(B * T, hc), g_ref) <= 1e-5
+    assert normwise(to_f64(y), y_ref) <= TOL[dtype] / (4 if dtype == "bf16" else 1)
+
+
+# ------------------------------------------------------------------ whole forward
+@pytest.mark.parametrize("name,n", [("tiny_fp32", None), ("b4_t1024", 160), ("b8_t4096", 48)])
+def test_forward_within_tolerance(eg, name, n):
+    c = case(name)
+    y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    sync()
+    N = c.B * c.T
+    pos = np.arange(N) if n is None else c.sample_positions(n, seed=3)
+    ref = c.y_at(pos)
+    err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], ref)
+    assert err <= TOL[c.w.dtype], err
+
+
+def test_forward_is_deterministic(eg):
+    c = case("b4_t1024")
+    ws = eg.alloc_workspace(c.cfg())
+    y1 = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"], workspace=ws).clone()
+    y2 = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"], workspace=ws)
+    sync()
+    assert torch.equal(y1, y2)
+
+
+def test_forward_errors(eg):
+    import hashed_gram_conditional_amd as m
+
+    c = case("tiny_fp32")
+    cfg = c.cfg()
+    ws = eg.alloc_workspace(cfg)
+    with pytest.raises(m.EngramError) as ei:
+        eg.forward(cfg, c.params, c.dev["ids"], c.dev["hidden"], workspace=ws[:128])
+    assert ei.value.status == -2
+    bad = c.cfg()
+    bad.orders[1] = 2            # not ascending
+    with pytest.raises(m.EngramError) as ei:
+        eg.forward(bad, c.params, c.dev["ids"], c.dev["hidden"], workspace=ws)
+    assert ei.value.status == -1
+    # empty batch succeeds without work
+    eg.forward(c.cfg(0, 64), c.params, c.dev["ids"], c.dev["hidden"], workspace=ws)
+
+
+# ------------------------------------------------------------------ state: chunked prefill and decode
+def test_chunked_prefill_matches_single_prefill(eg):
+    c = case("b4_t1024")
+    full = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    st = eg.State(c.cfg(), c.B)
+    outs = []
+    t0 = 0
+    for L in (1, 2, 7, 100, 300, 614):
+        ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+        hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+        outs.append(eg.forward(c.cfg(c.B, L), c.params, ids, hid, state=st))
+        t0 += L
+    sync()
+    assert t0 == c.T
+    chunked = torch.cat(outs, dim=1)
+    assert torch.equal(chunked, full)
+    assert st.n_past.cpu().tolist() == [c.T] * c.B
+
+
+def test_decode_matches_oracle(eg):
+    """Decode-shaped workload: prompt prefill, then single-token steps with state;
+    each step's output must equal the oracle's prefill over the whole sequence."""
+    c = case("decode_b256", decode_steps=64)
+    w = c.w
+    P = w.decode_prompt
+    cfgp = c.cfg(c.B, P)
+    cfg1 = c.cfg(c.B, 1)
+    ids, hid = c.dev["ids"], c.dev["hidden"]
+    st = eg.State(cfg1, c.B)
+    ws = eg.alloc_workspace(cfgp)
+    outs = [eg.forward(cfgp, c.params, ids[:, :P].contiguous(), hid[:, :P].contiguous(), state=st, workspace=ws)]
+    steps_ids = ids[:, P:].t().contiguous()
+    steps_hid = hid[:, P:].transpose(0, 1).contiguous()
+    for s in range(w.decode_steps):
+        outs.append(eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=st, workspace=ws))
+    sync()
+    y = torch.cat(outs, dim=1)                                   # [B][P+steps][hc][d]
+    # equals one prefill over the whole sequence on the GPU
+    whole = eg.forward(c.cfg(), c.params, ids, hid)
+    sync()
+    assert normwise(to_f64(y), to_f64(whole)) <= 1e-6
+    rng = np.random.default_rng(4)
+    b = rng.choice(c.B, size=8, replace=False)
+    t = np.concatenate([[0, P - 1, P], rng.choice(np.arange(P + 1, c.T), size=5, replace=False)])
+    pos = (b[:, None] * c.T + t[None, :]).ravel()
+    ref = c.y_at(pos)
+    got = to_f64(y).reshape(c.B * c.T, w.hc_mult, w.hidden)[pos]
+    assert normwise(got, ref) <= TOL[w.dtype]

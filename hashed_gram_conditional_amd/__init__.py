@@ -15,7 +15,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-from ._build import LIB_PATH, build  # noqa: F401
+from ._build import LIB_PATH, build, source_hash  # noqa: F401
 
 MAX_ORDERS = 8
 MAX_HEADS = 64

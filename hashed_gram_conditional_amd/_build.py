@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(PKG, "libengram.so")
 SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gate_conv.hip"]
 HEADERS = ["engram_internal.h", os.path.join("..", "..", "include", "engram.h")]
 
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-shared", "-std=c++17", "-Wall",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-shared", "-std=c++20", "-Wall",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-I" + os.path.join(ROOT, "include")]
 

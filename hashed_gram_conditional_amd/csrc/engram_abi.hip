@@ -85,28 +85,50 @@ engram_status hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : EN
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// engram_forward runs the fused path (projection GEMM with the gate sums in
+// its epilogue, then a small finalize kernel) when the weights are bf16 and the
+// GEMM's channel tile divides the hidden size; otherwise the projections are
+// stored and a separate gate kernel reads them back.
+int fused_tile(const engram_config* c) {
+  if (c->dtype != ENGRAM_BF16) return 0;
+  const int64_t N = (int64_t)c->batch * c->seqlen;
+  return gemm_gate_tile_n(N, (c->hc_mult + 1) * c->hidden, (int)emb_dim(c), c->hidden);
+}
+
 struct Workspace {
-  void* e;
-  void* kv;
-  float* g;
+  void* e;         // [N][E]
+  void* kv;        // unfused: [N][hc+1][d]
+  void* v;         // fused: [N][d]
+  float4* part;    // fused: [N][hc][d / tile]
+  float* g;        // [N][hc]
   size_t bytes;
 };
 
 Workspace carve(const engram_config* c, void* base) {
   const int64_t N = (int64_t)c->batch * c->seqlen;
-  Workspace w;
+  const int tile = fused_tile(c);
+  Workspace w = {};
   size_t off = 0;
-  w.e = (uint8_t*)base + off;
-  off += align_up((size_t)N * emb_dim(c) * esize(c));
-  w.kv = (uint8_t*)base + off;
-  off += align_up((size_t)N * (c->hc_mult + 1) * c->hidden * esize(c));
-  w.g = (float*)((uint8_t*)base + off);
-  off += align_up((size_t)N * c->hc_mult * sizeof(float));
+  auto take = [&](size_t n) {
+    void* p = (uint8_t*)base + off;
+    off += align_up(n);
+    return p;
+  };
+  w.e = take((size_t)N * emb_dim(c) * esize(c));
+  if (tile) {
+    w.v = take((size_t)N * c->hidden * esize(c));
+    w.part = (float4*)take((size_t)N * c->hc_mult * (c->hidden / tile) * sizeof(float4));
+  } else {
+    w.kv = take((size_t)N * (c->hc_mult + 1) * c->hidden * esize(c));
+  }
+  w.g = (float*)take((size_t)N * c->hc_mult * sizeof(float));
   w.bytes = off;
   return w;
 }
 
 const char* const kForwardKernels[] = {"hash_gather", "project_gemm", "gate", "short_conv", "advance_state"};
+const char* const kFusedKernels[] = {"hash_gather", "project_gate_gemm", "gate_finalize", "short_conv",
+                                     "advance_state"};
 
 GatherArgs gather_args(const engram_config* c, const engram_params* p, const int32_t* ids, const engram_state* st) {
   GatherArgs a;
@@ -150,11 +172,12 @@ GateArgs gate_args(const engram_config* c, const engram_params* p, const void* k
   return a;
 }
 
-ConvArgs conv_args(const engram_config* c, const engram_params* p, const void* kv, const float* g, void* out,
-                   const engram_state* st) {
+// value rows: the last block of kv rows (stride (hc+1)*d), or a [N][d] array
+ConvArgs conv_args(const engram_config* c, const engram_params* p, const void* v, int64_t v_stride, const float* g,
+                   void* out, const engram_state* st) {
   ConvArgs a;
-  a.v = (const uint8_t*)kv + (int64_t)c->hc_mult * c->hidden * esize(c);
-  a.v_stride = (int64_t)(c->hc_mult + 1) * c->hidden;
+  a.v = v;
+  a.v_stride = v_stride;
   a.g = g;
   a.conv_w = p->conv_w;
   a.out = out;
@@ -210,14 +233,43 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   ga.e_out = (uint8_t*)w.e;
   if ((e = tm.before()) || (e = launch_hash_gather(hc, ga, true, s)) || (e = tm.after())) return hip_status(e);
 
-  const GemmArgs gm = gemm_args(c, p, w.e, w.kv);
-  if ((e = tm.before()) || (e = bf16 ? launch_gemm_bf16(gm, s) : launch_gemm_f32(gm, s)) || (e = tm.after()))
-    return hip_status(e);
+  const void* v;
+  int64_t v_stride;
+  if (w.kv == nullptr) {  // fused: projections with the gate sums, then g
+    GemmGateArgs gg;
+    gg.g = gemm_args(c, p, w.e, nullptr);
+    gg.hidden = hidden;
+    gg.gamma_k = p->gamma_k;
+    gg.gamma_q = p->gamma_q;
+    gg.v_out = w.v;
+    gg.partials = w.part;
+    gg.hc = c->hc_mult;
+    gg.d = c->hidden;
+    if ((e = tm.before()) || (e = launch_gemm_gate_bf16(gg, s)) || (e = tm.after())) return hip_status(e);
+    GateFinalizeArgs gf;
+    gf.partials = w.part;
+    gf.g_out = w.g;
+    gf.n_tok = (int32_t)N;
+    gf.hc = c->hc_mult;
+    gf.d = c->hidden;
+    gf.n_part = c->hidden / fused_tile(c);
+    gf.eps = c->norm_eps;
+    gf.clamp = c->gate_clamp;
+    gf.inv_sqrt_d = (float)(1.0 / sqrt((double)c->hidden));
+    if ((e = tm.before()) || (e = launch_gate_finalize(gf, s)) || (e = tm.after())) return hip_status(e);
+    v = w.v;
+    v_stride = c->hidden;
+  } else {
+    const GemmArgs gm = gemm_args(c, p, w.e, w.kv);
+    if ((e = tm.before()) || (e = bf16 ? launch_gemm_bf16(gm, s) : launch_gemm_f32(gm, s)) || (e = tm.after()))
+      return hip_status(e);
+    const GateArgs gt = gate_args(c, p, w.kv, hidden, w.g);
+    if ((e = tm.before()) || (e = launch_gate(gt, s)) || (e = tm.after())) return hip_status(e);
+    v = (const uint8_t*)w.kv + (int64_t)c->hc_mult * c->hidden * esize(c);
+    v_stride = (int64_t)(c->hc_mult + 1) * c->hidden;
+  }
 
-  const GateArgs gt = gate_args(c, p, w.kv, hidden, w.g);
-  if ((e = tm.before()) || (e = launch_gate(gt, s)) || (e = tm.after())) return hip_status(e);
-
-  const ConvArgs cv = conv_args(c, p, w.kv, w.g, out, st);
+  const ConvArgs cv = conv_args(c, p, v, v_stride, w.g, out, st);
   if ((e = tm.before()) || (e = launch_conv(cv, s)) || (e = tm.after())) return hip_status(e);
 
   if (st) {
@@ -320,7 +372,9 @@ engram_status engram_gate_conv(const engram_config* cfg, const engram_params* pr
   if (!aligned(kv, 16) || !aligned(hidden, 16) || !aligned(out, 16) || !aligned(g_out, 4)) return ENGRAM_EINVAL;
   hipError_t e = launch_gate(gate_args(cfg, prm, kv, hidden, g_out), stream);
   if (e) return hip_status(e);
-  return hip_status(launch_conv(conv_args(cfg, prm, kv, g_out, out, st), stream));
+  const void* v = (const uint8_t*)kv + (int64_t)cfg->hc_mult * cfg->hidden * esize(cfg);
+  return hip_status(launch_conv(conv_args(cfg, prm, v, (int64_t)(cfg->hc_mult + 1) * cfg->hidden, g_out, out, st),
+                                stream));
 }
 
 engram_status engram_forward(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
@@ -340,7 +394,7 @@ engram_status engram_forward_timed(const engram_config* cfg, const engram_params
 
 const char* engram_forward_kernel_name(const engram_config* cfg, int32_t i) {
   if (validate(cfg) || i < 0 || i >= 5) return nullptr;
-  return kForwardKernels[i];
+  return fused_tile(cfg) ? kFusedKernels[i] : kForwardKernels[i];
 }
 
 const char* engram_status_string(engram_status s) {

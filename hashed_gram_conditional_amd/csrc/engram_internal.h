@@ -73,6 +73,33 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
+// Projection GEMM with the gate reductions in its epilogue (bf16).  Key tiles
+// are not stored: each writes, per token, the partial sums (sum K^2, sum Q^2,
+// sum K gk gq Q) over its channels; value tiles are stored to v_out.
+struct GemmGateArgs {
+  GemmArgs g;             // C unused
+  const void* hidden;     // [M][hc][d] queries
+  const void* gamma_k;    // [hc][d]
+  const void* gamma_q;    // [hc][d]
+  void* v_out;            // [M][d]
+  float4* partials;       // [M][hc][n_part] (x = sum K^2, y = sum Q^2, z = sum K gk gq Q)
+  int32_t hc, d;
+};
+
+// channel tile width of the fused GEMM for this shape (the partials per
+// (token, branch) are d / width), or 0 when the fused path does not apply
+int gemm_gate_tile_n(int64_t M, int N, int K, int d);
+hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s);
+
+// g[n][h] from the partial sums of the fused GEMM
+struct GateFinalizeArgs {
+  const float4* partials;  // [N][hc][n_part]
+  float* g_out;            // [N][hc]
+  int32_t n_tok, hc, d, n_part;
+  float eps, clamp, inv_sqrt_d;
+};
+hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------- gate / conv
 struct GateArgs {
   const void* kv;        // [N][hc+1][d]

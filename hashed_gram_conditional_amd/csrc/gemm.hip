@@ -13,11 +13,18 @@
 // consecutive output channels of one token and the epilogue stores 8 bytes at
 // a time along the contiguous channel axis.
 //
-// Tiling: 128 tokens x 128 channels per 256-thread workgroup (2x2 waves of
-// 64x64, each a 2x2 grid of 32x32 MFMA tiles), K step 64, double-buffered LDS
-// (64 KB) with one barrier per K step.  LDS rows are 128 bytes; the 16-byte
-// piece c of row r is stored at piece c ^ ((r >> 1) & 7), so the 16 lanes of a
-// ds_read_b128 phase (16 rows, same logical piece) hit 16 distinct bank groups.
+// Tiling: up to 256 tokens x 256 channels per 256-thread workgroup (2x2 waves,
+// each a grid of 32x32 MFMA tiles, 128x128 per wave at the largest tile, with
+// the 256 accumulators per lane in AGPRs), K step 64, double-buffered LDS
+// (128 KB at the largest tile) with one barrier per K step.  A wave tile of
+// 128x128 needs half the LDS read bandwidth per MFMA of a 64x64 one, and a
+// 256x256 workgroup tile a quarter of the L2 traffic per flop of a 128x128
+// one.  LDS rows are 128 bytes; the 16-byte piece c of row r is stored at
+// piece c ^ ((r >> 1) & 7), so the 16 lanes of a ds_read_b128 phase (16 rows,
+// same logical piece) hit 16 distinct bank groups.
+#include <type_traits>
+#include <utility>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -25,118 +32,330 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;  // tokens per tile
-constexpr int BN = 128;  // output channels per tile
-constexpr int BK = 64;   // reduction step
-constexpr int kThreads = 256;
-constexpr int kPieces = BK / 8;  // 16-byte pieces per LDS row
+constexpr int kThreads = 256;          // 4 waves, 2 x 2 over the tile
 
-__device__ __forceinline__ int swz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+#ifndef ENGRAM_GEMM_BK
+#define ENGRAM_GEMM_BK 64
+#endif
+#ifndef ENGRAM_GEMM_STAGES
+#define ENGRAM_GEMM_STAGES 2
+#endif
+constexpr int BK = ENGRAM_GEMM_BK;           // reduction step (bf16 elements)
+constexpr int kPieces = BK / 8;              // 16-byte pieces per LDS row
+constexpr int kStages = ENGRAM_GEMM_STAGES;  // LDS ring depth
+constexpr int kRowsPerDma = 64 / kPieces;    // rows one 1 KB DMA instruction fills
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-__global__ void __launch_bounds__(kThreads, 2) k_gemm_bf16(GemmArgs a) {
-  __shared__ uint4 sA[2][BM * kPieces];  // e tile
-  __shared__ uint4 sB[2][BN * kPieces];  // weight tile
+// Physical 16-byte piece of logical piece `piece` in LDS row `row`.  LDS reads
+// are served 256 bytes (64 banks) at a time, i.e. 16 lanes of a ds_read_b128;
+// those lanes read 16 consecutive rows at the same logical piece, and the XOR
+// spreads them over 16 distinct 16-byte bank groups (0 bank conflicts
+// measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ int swz(int row, int piece) {
+  if constexpr (kPieces == 8) return piece ^ ((row >> 1) & 7);   // 128-byte rows: 2 rows per bank line
+  else return piece ^ ((row >> 2) & 3);                          // 64-byte rows: 4 rows per bank line
+}
+
+// Logical tile of a workgroup.  Workgroups are dispatched round-robin over the
+// 8 XCDs, so workgroup b runs on XCD b % 8; each XCD is given a contiguous
+// range of logical tiles, ordered GROUP m-tiles at a time with the channel
+// tiles innermost, so the tiles resident on one XCD share a few token slabs
+// and weight slabs in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& mt, int& nt) {
+  constexpr int GROUP = 4;
+  const int total = m_tiles * n_tiles;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int L = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int span = GROUP * n_tiles;
+  const int first_m = (L / span) * GROUP;
+  const int gsz = min(m_tiles - first_m, GROUP);
+  const int r = L - (L / span) * span;
+  mt = first_m + r % gsz;
+  nt = r / gsz;
+}
+
+// Buffer resource over rows [row0, row0 + rows) of a K-contiguous bf16 matrix:
+// loads past the last valid row, or at an offset marked out of range, return
+// zero, so ragged tiles and the K tail need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t row0, int64_t rows, int K) {
+  const int64_t bytes = rows * (int64_t)K * 2;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * K), (short)0, (int)(bytes > 0 ? bytes : 0),
+                                           0x00020000);
+}
+
+constexpr int kOutOfRange = (int)0x80000000;
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 4 consecutive bf16 of a row as floats
+__device__ __forceinline__ void load4(const uint16_t* p, float* v) {
+  const uint2 u = *(const uint2*)p;
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+
+// BM tokens x BN channels per workgroup; each wave owns (BM/2) x (BN/2) as a
+// grid of 32x32 MFMA tiles.  MFMA A = weight rows (channels), B = e rows
+// (tokens), so accumulator r of tile (i, j) is channel
+//   n0 + wn*BN/2 + 32 i + 8 (r/4) + 4 (lane/32) + r%4   of token   m0 + wm*BM/2 + 32 j + lane%32.
+//
+// Operands move global -> LDS by buffer_load_dwordx4 ... lds (no staging
+// registers): one instruction of one wave fills 1 KB of LDS in lane order, so
+// each lane fetches the global piece whose swizzled LDS slot is its own.  A
+// ring of kStages LDS stages keeps kStages-1 K steps of loads in flight; every
+// step issues exactly one more step of loads (past the end: out-of-range loads
+// that only write zeros into a stage nobody reads again) so the wait before
+// each step is one constant vmcnt, followed by a barrier that makes the other
+// waves' loads visible.  The K steps are padded to a multiple of kStages with
+// all-zero steps and the loop is unrolled over the ring, so every stage index
+// is a constant and the compiler can tell the stage being filled from the one
+// being read (it then inserts no wait of its own between them).  Within a step
+// the fragments of slice kk+1 are read while the MFMAs of slice kk run.
+//
+// GATE = false: the tile is stored to C (bf16).
+// GATE = true (fused gate): a tile of branch h's key channels is not stored;
+// its epilogue reads the matching tile of the hidden state Q (the query of
+// branch h) and the two RMSNorm scales, and writes per token the partial sums
+// over its BN channels of K^2, Q^2 and K gk gq Q -- everything the gate needs
+// from K (formula sheet, kwkr.cn/news/37585, section 2.2 step 1: the gate is
+// the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
+// square).  Value tiles are stored to v_out.  Writing K and reading it back
+// is the largest traffic of the unfused path.
+template <int BM, int BN, bool GATE>
+__global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
+  constexpr int TM = BM / 64, TN = BN / 64;            // MFMA tiles per wave along tokens / channels
+  constexpr int QA = BM / (4 * kRowsPerDma);           // DMA instructions per wave per K step
+  constexpr int QB = BN / (4 * kRowsPerDma);
+  constexpr int kPerStep = QA + QB;
+  __shared__ u32x4 sA[kStages][BM * kPieces];          // e tiles
+  __shared__ u32x4 sB[kStages][BN * kPieces];          // weight tiles
+  const GemmArgs& a = ga.g;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1;   // token half of the tile
-  const int wn = wave >> 1;  // channel half of the tile
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const uint16_t* __restrict__ A = (const uint16_t*)a.A;
-  const uint16_t* __restrict__ B = (const uint16_t*)a.B;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
+  int mt, nt;
+  tile_of(blockIdx.x, m_tiles, n_tiles, mt, nt);
+  const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
   const int K = a.K;
   const int nk = (K + BK - 1) / BK;
+  const int nk_pad = (nk + kStages - 1) / kStages * kStages;
+  const __amdgpu_buffer_rsrc_t rA = tile_rsrc((const uint16_t*)a.A, m0, min((int64_t)BM, a.M - m0), K);
+  const __amdgpu_buffer_rsrc_t rB = tile_rsrc((const uint16_t*)a.B, n0, min((int64_t)BN, a.N - n0), K);
+  const int row_bytes = K * 2;
 
-  // global -> register staging: 4 pieces of A and 4 of B per thread per K step
-  uint4 ra[4], rb[4];
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BK;
+  // this lane's slot in the block of rows one DMA instruction fills: tile row
+  // (q*4 + wave)*kRowsPerDma + drow for instruction q; the q term moves the row
+  // by a multiple of 32, which leaves the swizzle unchanged
+  const int drow = wave * kRowsPerDma + lane / kPieces;
+  const int dlog = swz(drow, lane % kPieces);          // logical piece it fetches (swz is its own inverse)
+  const int dvoff = drow * row_bytes + dlog * 16;
+
+  auto issue = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int voff = (kt < nk && kt * BK + dlog * 8 < K) ? dvoff + kt * BK * 2 : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, piece = c & 7;
-      const int k = k0 + piece * 8;
-      const int64_t m = m0 + row, n = n0 + row;
-      ra[i] = (m < a.M && k < K) ? *(const uint4*)(A + m * K + k) : make_uint4(0, 0, 0, 0);
-      rb[i] = (n < a.N && k < K) ? *(const uint4*)(B + n * K + k) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
+    for (int q = 0; q < QA; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(&sA[S][(q * 4 + wave) * 64]), 16, voff,
+                                               q * 4 * kRowsPerDma * row_bytes, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, piece = c & 7;
-      sA[buf][row * kPieces + swz(row, piece)] = ra[i];
-      sB[buf][row * kPieces + swz(row, piece)] = rb[i];
-    }
+    for (int q = 0; q < QB; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&sB[S][(q * 4 + wave) * 64]), 16, voff,
+                                               q * 4 * kRowsPerDma * row_bytes, 0, 0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[TN][TM];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < TN; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < TM; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  for (int kt = 0; kt < nk; kt++) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
+  // fragments of one 16-wide k slice: TN weight fragments, TM e fragments
+  auto load_frags = [&](auto stage_tag, int kk, bf16x8* fa, bf16x8* fb) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int piece = kk * 2 + lhalf;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; kk++) {
-      const int piece = kk * 2 + lhalf;
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const int r = wn * 64 + i * 32 + lrow;
-        fa[i] = as_bf16x8(sB[buf][r * kPieces + swz(r, piece)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int r = wm * 64 + j * 32 + lrow;
-        fb[j] = as_bf16x8(sA[buf][r * kPieces + swz(r, piece)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TN; i++) {
+      const int r = wn * (BN / 2) + i * 32 + lrow;
+      fa[i] = __builtin_bit_cast(bf16x8, sB[S][r * kPieces + swz(r, piece)]);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+      const int r = wm * (BM / 2) + j * 32 + lrow;
+      fb[j] = __builtin_bit_cast(bf16x8, sA[S][r * kPieces + swz(r, piece)]);
+    }
+  };
+  auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+      for (int j = 0; j < TM; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // One K step; sched_barrier keeps the scheduler from sinking the reads of
+  // the next slice back next to their use.
+  auto step = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    // at most kStages-2 steps of this wave's loads may remain: step kt has landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kPerStep));
+    __builtin_amdgcn_s_barrier();
+    bf16x8 fa0[TN], fb0[TM], fa1[TN], fb1[TM];
+    load_frags(stage_tag, 0, fa0, fb0);
+    // refill the stage every wave finished reading before the barrier
+    issue(std::integral_constant<int, (S + kStages - 1) % kStages>{}, kt + kStages - 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; kk += 2) {
+      if (kk + 1 < BK / 16) load_frags(stage_tag, kk + 1, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < BK / 16) {
+        if (kk + 2 < BK / 16) load_frags(stage_tag, kk + 2, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
-  // epilogue: accumulator r of tile (i, j) is output channel
-  // n0 + wn*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4 of token m0 + wm*64 + j*32 + lane%32
-  uint16_t* __restrict__ C = (uint16_t*)a.C;
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (issue(std::integral_constant<int, I>{}, I), ...);
+  }(std::make_integer_sequence<int, kStages - 1>{});
+  for (int kt = 0; kt < nk_pad; kt += kStages) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(std::integral_constant<int, I>{}, kt + I), ...);
+    }(std::make_integer_sequence<int, kStages>{});
+  }
+  // drain the trailing out-of-range loads before the workgroup's LDS is reused or released
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // plain store of a tile: 4 consecutive channels (8 bytes) per store
+  auto store_tile = [&](uint16_t* __restrict__ C, int64_t ldc, int64_t col0, int64_t ncols) {
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int64_t m = m0 + wm * 64 + j * 32 + lrow;
-    if (m >= a.M) continue;
+    for (int j = 0; j < TM; j++) {
+      const int64_t m = m0 + wm * (BM / 2) + j * 32 + lrow;
+      if (m >= a.M) continue;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+      for (int i = 0; i < TN; i++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int64_t n = col0 + wn * (BN / 2) + i * 32 + 8 * q + 4 * lhalf;
+          if (n >= ncols) continue;
+          const bf16x4 v = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1],
+                            (__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
+          *(bf16x4*)(C + m * ldc + n) = v;
+        }
+      }
+    }
+  };
+
+  if constexpr (!GATE) {
+    store_tile((uint16_t*)a.C, a.N, n0, a.N);
+  } else {
+    const int d = ga.d, hc = ga.hc;
+    const int h = (int)(n0 / d);
+    if (h >= hc) {  // value tile
+      store_tile((uint16_t*)ga.v_out, d, n0 - (int64_t)hc * d, d);
+      return;
+    }
+    // key tile of branch h: channels c0 .. c0+BN-1 of the branch
+    const int c0 = (int)(n0 - (int64_t)h * d);
+    const int cw = c0 + wn * (BN / 2) + 4 * lhalf;   // + 32 i + 8 q + e
+    const uint16_t* gk = (const uint16_t*)ga.gamma_k + (int64_t)h * d + cw;
+    const uint16_t* gq = (const uint16_t*)ga.gamma_q + (int64_t)h * d + cw;
+    const uint16_t* q_rows[TM];
+    float kk[TM], qq[TM], kq[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+      const int64_t m = min(m0 + wm * (BM / 2) + j * 32 + lrow, (int64_t)a.M - 1);  // rows past M: any valid row, discarded below
+      q_rows[j] = (const uint16_t*)ga.hidden + (m * hc + h) * (int64_t)d + cw;
+      kk[j] = qq[j] = kq[j] = 0.f;
+    }
+    // per token: sums over this lane's 16 runs of 4 channels
+#pragma unroll
+    for (int i = 0; i < TN; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int64_t n = n0 + wn * 64 + i * 32 + 8 * q + 4 * lhalf;
-        if (n >= a.N) continue;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc[i][j][4 * q + 0]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc[i][j][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 3]) << 16);
-        *(uint2*)(C + m * a.N + n) = pk;
+        float x[4], y[4], g[4];
+        load4(gk + 32 * i + 8 * q, x);
+        load4(gq + 32 * i + 8 * q, y);
+#pragma unroll
+        for (int e = 0; e < 4; e++) g[e] = x[e] * y[e];
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+          float qv[4];
+          load4(q_rows[j] + 32 * i + 8 * q, qv);
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float k = acc[i][j][4 * q + e];
+            kk[j] = fmaf(k, k, kk[j]);
+            qq[j] = fmaf(qv[e], qv[e], qq[j]);
+            kq[j] = fmaf(k * g[e], qv[e], kq[j]);
+          }
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+      // lanes l and l+32 hold the other half of the wave's channels of the same token
+      kk[j] += __shfl_xor(kk[j], 32, 64);
+      qq[j] += __shfl_xor(qq[j], 32, 64);
+      kq[j] += __shfl_xor(kq[j], 32, 64);
+    }
+    // the two waves of a token row (wn = 0, 1) meet in LDS; the operand stages are free now
+    __syncthreads();
+    float4* red = reinterpret_cast<float4*>(&sA[0][0]);   // [wm][j][lrow] of wave wn = 1
+    if (wn == 1 && lhalf == 0)
+#pragma unroll
+      for (int j = 0; j < TM; j++) red[(wm * TM + j) * 32 + lrow] = make_float4(kk[j], qq[j], kq[j], 0.f);
+    __syncthreads();
+    if (wn == 0 && lhalf == 0) {
+      const int n_part = d / BN, part = c0 / BN;
+#pragma unroll
+      for (int j = 0; j < TM; j++) {
+        const int64_t m = m0 + wm * (BM / 2) + j * 32 + lrow;
+        if (m >= a.M) continue;
+        const float4 o = red[(wm * TM + j) * 32 + lrow];
+        ga.partials[(m * hc + h) * n_part + part] = make_float4(kk[j] + o.x, qq[j] + o.y, kq[j] + o.z, 0.f);
       }
     }
   }
+}
+
+// g from the fused GEMM's partial sums: one thread per (token, branch)
+__global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.n_tok * a.hc) return;
+  const float4* p = a.partials + i * a.n_part;
+  float kk = 0.f, qq = 0.f, kq = 0.f;
+  for (int t = 0; t < a.n_part; t++) {
+    const float4 v = p[t];
+    kk += v.x;
+    qq += v.y;
+    kq += v.z;
+  }
+  const float inv_d = 1.f / (float)a.d;
+  const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
+  const float rq = 1.f / sqrtf(qq * inv_d + a.eps);
+  const float s = kq * rk * rq * a.inv_sqrt_d;
+  const float sgn = s > 0.f ? 1.f : (s < 0.f ? -1.f : 0.f);
+  const float act = sgn * sqrtf(fmaxf(fabsf(s), a.clamp));
+  a.g_out[i] = 1.f / (1.f + expf(-act));
 }
 
 // float32 path: a plain LDS-tiled FMA GEMM, 64x64 tile, 4x4 outputs per thread.
@@ -180,10 +399,47 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
 
 }  // namespace
 
+template <int BM, int BN, bool GATE>
+hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
+  const int64_t tiles = (int64_t)((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
+  k_gemm_bf16<BM, BN, GATE><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// the largest tile that still gives every CU a few workgroups
+static int pick_tile_n(int64_t M, int N) {
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  return big >= 4 * 256 ? 256 : 128;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-  k_gemm_bf16<<<grid, kThreads, 0, s>>>(a);
+  GemmGateArgs ga = {};
+  ga.g = a;
+  const int64_t mid = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
+  if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, false>(ga, s);
+  if (mid >= 2 * 256) return gemm_launch<256, 128, false>(ga, s);
+  return gemm_launch<128, 128, false>(ga, s);
+}
+
+int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
+  (void)K;
+  const int bn = pick_tile_n(M, N);
+  return (d % bn == 0) ? bn : 0;
+}
+
+hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
+  if (a.g.M == 0 || a.g.N == 0) return hipSuccess;
+  const int bn = gemm_gate_tile_n(a.g.M, a.g.N, a.g.K, a.d);
+  if (bn == 256) return gemm_launch<256, 256, true>(a, s);
+  if (bn == 128) return gemm_launch<256, 128, true>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_tok * a.hc;
+  if (n == 0) return hipSuccess;
+  k_gate_finalize<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

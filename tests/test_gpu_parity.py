@@ -285,10 +285,12 @@ def test_decode_matches_oracle(eg):
         outs.append(eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=st, workspace=ws))
     sync()
     y = torch.cat(outs, dim=1)                                   # [B][P+steps][hc][d]
-    # equals one prefill over the whole sequence on the GPU
+    # equals one prefill over the whole sequence on the GPU, up to bf16 output
+    # rounding: a step of 256 tokens and the whole prefill may pick different
+    # GEMM channel tiles, which sum the gate's partial sums in another order
     whole = eg.forward(c.cfg(), c.params, ids, hid)
     sync()
-    assert normwise(to_f64(y), to_f64(whole)) <= 1e-6
+    assert normwise(to_f64(y), to_f64(whole)) <= 1e-2
     rng = np.random.default_rng(4)
     b = rng.choice(c.B, size=8, replace=False)
     t = np.concatenate([[0, P - 1, P], rng.choice(np.arange(P + 1, c.T), size=5, replace=False)])

@@ -102,6 +102,37 @@ __global__ void __launch_bounds__(256) k_gate(GateArgs a) {
 
 constexpr int kConvIters = 16;  // positions a thread walks (stride D)
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements as raw words (bf16: one 16-byte piece in lo; f32:
+// two pieces, lo and hi)
+template <bool BF16>
+__device__ __forceinline__ void load_raw8(const void* p, int64_t i, u32x4& lo, u32x4& hi) {
+  if constexpr (BF16) {
+    lo = *(const u32x4*)((const uint16_t*)p + i);
+  } else {
+    lo = *(const u32x4*)((const float*)p + i);
+    hi = *(const u32x4*)((const float*)p + i + 4);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const u32x4& lo, const u32x4& hi, float scale, float* v) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v[2 * k] = __uint_as_float(lo[k] << 16) * scale;
+      v[2 * k + 1] = __uint_as_float(lo[k] & 0xFFFF0000u) * scale;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v[k] = __uint_as_float(lo[k]) * scale;
+      v[4 + k] = __uint_as_float(hi[k]) * scale;
+    }
+  }
+}
+
 template <bool BF16, int KS>
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int groups = a.d >> 3;
@@ -120,10 +151,26 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int b = y / runs;
   const int t_first = run * run_len + r;
   if (t_first >= T) return;
+  const int n_it = min(kConvIters, (T - t_first + D - 1) / D);   // positions this thread visits
 
   const int64_t d = a.d;
   const int R = (KS - 1) * D;
   const int64_t past = a.n_past ? a.n_past[b] : 0;
+
+  // every V slice and gate of the walk is loaded before any is used, so a
+  // thread keeps up to kConvIters independent loads in flight
+  u32x4 lo[kConvIters], hi[kConvIters];
+  float gv[kConvIters];
+#pragma unroll
+  for (int it = 0; it < kConvIters; it++) {
+    lo[it] = hi[it] = u32x4{0, 0, 0, 0};
+    gv[it] = 0.f;
+    if (it < n_it) {
+      const int64_t n = (int64_t)b * T + t_first + it * D;
+      load_raw8<BF16>(a.v, n * a.v_stride + c0, lo[it], hi[it]);
+      gv[it] = a.g[n * a.hc + h];
+    }
+  }
 
   float w[KS][8];  // taps of channel c0+i: conv_w[h][c0+i][0..KS)
 #pragma unroll
@@ -131,39 +178,40 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
 
-  // gated value at position t of this sequence (t may be negative: history)
-  auto vg_at = [&](int t, float* out) {
-    float g;
+  // gated value at a position before this walk's first one (from the rows of
+  // this call, the decode rings, or zero before the sequence start)
+  auto vg_before = [&](int t, float* out) {
     if (t >= 0) {
       const int64_t n = (int64_t)b * T + t;
-      load8(a.v, n * a.v_stride + c0, BF16, out);
-      g = a.g[n * a.hc + h];
-    } else {
-      const int64_t p = past + t;
-      if (p < 0 || a.v_ring == nullptr) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) out[i] = 0.f;
-        return;
-      }
-      const int64_t slot = (int64_t)b * R + p % R;
-      load8(a.v_ring, slot * d + c0, BF16, out);
-      g = a.g_ring[slot * a.hc + h];
+      u32x4 l, u;
+      load_raw8<BF16>(a.v, n * a.v_stride + c0, l, u);
+      unpack8<BF16>(l, u, a.g[n * a.hc + h], out);
+      return;
     }
+    const int64_t p = past + t;
+    if (p < 0 || a.v_ring == nullptr) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) out[i] *= g;
+      for (int i = 0; i < 8; i++) out[i] = 0.f;
+      return;
+    }
+    const int64_t slot = (int64_t)b * R + p % R;
+    u32x4 l, u;
+    load_raw8<BF16>(a.v_ring, slot * d + c0, l, u);
+    unpack8<BF16>(l, u, a.g_ring[slot * a.hc + h], out);
   };
 
   // hist[j] = Vg at t - (KS-1-j) D for j < KS-1
   constexpr int NH = KS > 1 ? KS - 1 : 1;
   float hist[NH][8];
 #pragma unroll
-  for (int j = 0; j < KS - 1; j++) vg_at(t_first - (KS - 1 - j) * D, hist[j]);
+  for (int j = 0; j < KS - 1; j++) vg_before(t_first - (KS - 1 - j) * D, hist[j]);
 
+#pragma unroll
   for (int it = 0; it < kConvIters; it++) {
+    if (it >= n_it) continue;
     const int t = t_first + it * D;
-    if (t >= T) break;
     float cur[8], out[8];
-    vg_at(t, cur);
+    unpack8<BF16>(lo[it], hi[it], gv[it], cur);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       float acc = fmaf(w[KS - 1][i], cur[i], cur[i]);

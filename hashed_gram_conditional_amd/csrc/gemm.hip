@@ -13,15 +13,12 @@
 // consecutive output channels of one token and the epilogue stores 8 bytes at
 // a time along the contiguous channel axis.
 //
-// Tiling: up to 256 tokens x 256 channels per 256-thread workgroup (2x2 waves,
-// each a grid of 32x32 MFMA tiles, 128x128 per wave at the largest tile, with
-// the 256 accumulators per lane in AGPRs), K step 64, double-buffered LDS
-// (128 KB at the largest tile) with one barrier per K step.  A wave tile of
-// 128x128 needs half the LDS read bandwidth per MFMA of a 64x64 one, and a
-// 256x256 workgroup tile a quarter of the L2 traffic per flop of a 128x128
-// one.  LDS rows are 128 bytes; the 16-byte piece c of row r is stored at
-// piece c ^ ((r >> 1) & 7), so the 16 lanes of a ds_read_b128 phase (16 rows,
-// same logical piece) hit 16 distinct bank groups.
+// Tiling: 256 tokens x 256 channels per workgroup of 8 waves (4 x 2, two per
+// SIMD, 64 x 128 per wave) for large shapes, 128 x 128 per workgroup of 4
+// waves for small ones, K step 64, two LDS stages filled by DMA.  LDS rows are
+// 128 bytes; the 16-byte piece c of row r is stored at piece c ^ ((r >> 1) & 7),
+// so the 16 lanes of a ds_read_b128 phase (16 rows, same logical piece) hit 16
+// distinct bank groups.
 #include <type_traits>
 #include <utility>
 
@@ -34,7 +31,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;          // 4 waves, 2 x 2 over the tile
 
 #ifndef ENGRAM_GEMM_BK
 #define ENGRAM_GEMM_BK 64
@@ -104,10 +100,10 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
   v[3] = __uint_as_float(u.y & 0xFFFF0000u);
 }
 
-// BM tokens x BN channels per workgroup; each wave owns (BM/2) x (BN/2) as a
-// grid of 32x32 MFMA tiles.  MFMA A = weight rows (channels), B = e rows
-// (tokens), so accumulator r of tile (i, j) is channel
-//   n0 + wn*BN/2 + 32 i + 8 (r/4) + 4 (lane/32) + r%4   of token   m0 + wm*BM/2 + 32 j + lane%32.
+// BM tokens x BN channels per workgroup of WM x WN waves; each wave owns
+// (BM/WM) x (BN/WN) as a grid of 32x32 MFMA tiles.  MFMA A = weight rows
+// (channels), B = e rows (tokens), so accumulator r of tile (i, j) is channel
+//   n0 + wn*BN/WN + 32 i + 8 (r/4) + 4 (lane/32) + r%4   of token   m0 + wm*BM/WM + 32 j + lane%32.
 //
 // Operands move global -> LDS by buffer_load_dwordx4 ... lds (no staging
 // registers): one instruction of one wave fills 1 KB of LDS in lane order, so
@@ -120,7 +116,9 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // all-zero steps and the loop is unrolled over the ring, so every stage index
 // is a constant and the compiler can tell the stage being filled from the one
 // being read (it then inserts no wait of its own between them).  Within a step
-// the fragments of slice kk+1 are read while the MFMAs of slice kk run.
+// the fragments of slice kk+1 are read, and one slice of the next step's
+// loads issued, while the MFMAs of slice kk run.  With 8 waves (2 per SIMD)
+// one wave's loads and barrier overlap the other wave's MFMAs.
 //
 // GATE = false: the tile is stored to C (bf16).
 // GATE = true (fused gate): a tile of branch h's key channels is not stored;
@@ -131,12 +129,14 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
 // square).  Value tiles are stored to v_out.  Writing K and reading it back
 // is the largest traffic of the unfused path.
-template <int BM, int BN, bool GATE>
-__global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
-  constexpr int TM = BM / 64, TN = BN / 64;            // MFMA tiles per wave along tokens / channels
-  constexpr int QA = BM / (4 * kRowsPerDma);           // DMA instructions per wave per K step
-  constexpr int QB = BN / (4 * kRowsPerDma);
+template <int BM, int BN, int WM, int WN, bool GATE>
+__global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) {
+  constexpr int NW = WM * WN;                          // waves
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // MFMA tiles per wave along tokens / channels
+  constexpr int QA = BM / (NW * kRowsPerDma);          // DMA instructions per wave per K step
+  constexpr int QB = BN / (NW * kRowsPerDma);
   constexpr int kPerStep = QA + QB;
+  constexpr int KK = BK / 16;                          // MFMA k slices per step
   __shared__ u32x4 sA[kStages][BM * kPieces];          // e tiles
   __shared__ u32x4 sB[kStages][BN * kPieces];          // weight tiles
   const GemmArgs& a = ga.g;
@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
   int mt, nt;
   tile_of(blockIdx.x, m_tiles, n_tiles, mt, nt);
@@ -157,23 +157,34 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
   const int row_bytes = K * 2;
 
   // this lane's slot in the block of rows one DMA instruction fills: tile row
-  // (q*4 + wave)*kRowsPerDma + drow for instruction q; the q term moves the row
-  // by a multiple of 32, which leaves the swizzle unchanged
+  // (q*NW + wave)*kRowsPerDma + drow for instruction q; the q term moves the
+  // row by a multiple of 32, which leaves the swizzle unchanged
+  static_assert((NW * kRowsPerDma) % 32 == 0, "swizzle period");
   const int drow = wave * kRowsPerDma + lane / kPieces;
   const int dlog = swz(drow, lane % kPieces);          // logical piece it fetches (swz is its own inverse)
   const int dvoff = drow * row_bytes + dlog * 16;
 
-  auto issue = [&](auto stage_tag, int kt) {
+  // instruction x of one step's loads: x < QA fills e rows, the rest weight rows
+  auto issue_one = [&](auto stage_tag, int voff, auto x_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    const int voff = (kt < nk && kt * BK + dlog * 8 < K) ? dvoff + kt * BK * 2 : kOutOfRange;
-#pragma unroll
-    for (int q = 0; q < QA; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(&sA[S][(q * 4 + wave) * 64]), 16, voff,
-                                               q * 4 * kRowsPerDma * row_bytes, 0, 0);
-#pragma unroll
-    for (int q = 0; q < QB; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&sB[S][(q * 4 + wave) * 64]), 16, voff,
-                                               q * 4 * kRowsPerDma * row_bytes, 0, 0);
+    constexpr int X = decltype(x_tag)::value;
+    if constexpr (X < QA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(&sA[S][(X * NW + wave) * 64]), 16, voff,
+                                               X * NW * kRowsPerDma * row_bytes, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&sB[S][((X - QA) * NW + wave) * 64]), 16, voff,
+                                               (X - QA) * NW * kRowsPerDma * row_bytes, 0, 0);
+  };
+  auto step_voff = [&](int kt) {
+    return (kt < nk && kt * BK + dlog * 8 < K) ? dvoff + kt * BK * 2 : kOutOfRange;
+  };
+  // loads [P*kPerStep/KK, (P+1)*kPerStep/KK) of a step into stage S
+  auto issue_part = [&](auto stage_tag, int voff, auto part_tag) {
+    constexpr int P = decltype(part_tag)::value;
+    constexpr int lo = P * kPerStep / KK, hi = (P + 1) * kPerStep / KK;
+    [&]<int... X>(std::integer_sequence<int, X...>) {
+      (issue_one(stage_tag, voff, std::integral_constant<int, lo + X>{}), ...);
+    }(std::make_integer_sequence<int, hi - lo>{});
   };
 
   f32x16 acc[TN][TM];
@@ -192,12 +203,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
     const int piece = kk * 2 + lhalf;
 #pragma unroll
     for (int i = 0; i < TN; i++) {
-      const int r = wn * (BN / 2) + i * 32 + lrow;
+      const int r = wn * (BN / WN) + i * 32 + lrow;
       fa[i] = __builtin_bit_cast(bf16x8, sB[S][r * kPieces + swz(r, piece)]);
     }
 #pragma unroll
     for (int j = 0; j < TM; j++) {
-      const int r = wm * (BM / 2) + j * 32 + lrow;
+      const int r = wm * (BM / WM) + j * 32 + lrow;
       fb[j] = __builtin_bit_cast(bf16x8, sA[S][r * kPieces + swz(r, piece)]);
     }
   };
@@ -208,34 +219,41 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
       for (int j = 0; j < TM; j++)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  // One K step; sched_barrier keeps the scheduler from sinking the reads of
-  // the next slice back next to their use.
+  // One K step; sched_barrier keeps the scheduler from regrouping the reads
+  // and loads of a slice with their uses.
   auto step = [&](auto stage_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
+    constexpr std::integral_constant<int, (S + kStages - 1) % kStages> next{};
     // at most kStages-2 steps of this wave's loads may remain: step kt has landed
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kPerStep));
     __builtin_amdgcn_s_barrier();
-    bf16x8 fa0[TN], fb0[TM], fa1[TN], fb1[TM];
-    load_frags(stage_tag, 0, fa0, fb0);
-    // refill the stage every wave finished reading before the barrier
-    issue(std::integral_constant<int, (S + kStages - 1) % kStages>{}, kt + kStages - 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; kk += 2) {
-      if (kk + 1 < BK / 16) load_frags(stage_tag, kk + 1, fa1, fb1);
+    const int voff = step_voff(kt + kStages - 1);
+    bf16x8 fa[2][TN], fb[2][TM];
+    load_frags(stage_tag, 0, fa[0], fb[0]);
+    // the stage being refilled was read by every wave before the barrier
+    auto slice = [&](auto part_tag) {
+      constexpr int P = decltype(part_tag)::value;
+      if constexpr (P + 1 < KK) load_frags(stage_tag, P + 1, fa[(P + 1) & 1], fb[(P + 1) & 1]);
+      issue_part(next, voff, part_tag);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(fa0, fb0);
+      mfmas(fa[P & 1], fb[P & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk + 1 < BK / 16) {
-        if (kk + 2 < BK / 16) load_frags(stage_tag, kk + 2, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    };
+    [&]<int... P>(std::integer_sequence<int, P...>) {
+      (slice(std::integral_constant<int, P>{}), ...);
+    }(std::make_integer_sequence<int, KK>{});
   };
 
+  // prologue: steps 0 .. kStages-2 in flight
+  auto issue_all = [&](auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int voff = step_voff(S);
+    [&]<int... X>(std::integer_sequence<int, X...>) {
+      (issue_one(stage_tag, voff, std::integral_constant<int, X>{}), ...);
+    }(std::make_integer_sequence<int, kPerStep>{});
+  };
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (issue(std::integral_constant<int, I>{}, I), ...);
+    (issue_all(std::integral_constant<int, I>{}), ...);
   }(std::make_integer_sequence<int, kStages - 1>{});
   for (int kt = 0; kt < nk_pad; kt += kStages) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -249,13 +267,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
   auto store_tile = [&](uint16_t* __restrict__ C, int64_t ldc, int64_t col0, int64_t ncols) {
 #pragma unroll
     for (int j = 0; j < TM; j++) {
-      const int64_t m = m0 + wm * (BM / 2) + j * 32 + lrow;
+      const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
       if (m >= a.M) continue;
 #pragma unroll
       for (int i = 0; i < TN; i++) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const int64_t n = col0 + wn * (BN / 2) + i * 32 + 8 * q + 4 * lhalf;
+          const int64_t n = col0 + wn * (BN / WN) + i * 32 + 8 * q + 4 * lhalf;
           if (n >= ncols) continue;
           const bf16x4 v = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1],
                             (__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
@@ -276,18 +294,18 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
     }
     // key tile of branch h: channels c0 .. c0+BN-1 of the branch
     const int c0 = (int)(n0 - (int64_t)h * d);
-    const int cw = c0 + wn * (BN / 2) + 4 * lhalf;   // + 32 i + 8 q + e
+    const int cw = c0 + wn * (BN / WN) + 4 * lhalf;   // + 32 i + 8 q + e
     const uint16_t* gk = (const uint16_t*)ga.gamma_k + (int64_t)h * d + cw;
     const uint16_t* gq = (const uint16_t*)ga.gamma_q + (int64_t)h * d + cw;
     const uint16_t* q_rows[TM];
     float kk[TM], qq[TM], kq[TM];
 #pragma unroll
     for (int j = 0; j < TM; j++) {
-      const int64_t m = min(m0 + wm * (BM / 2) + j * 32 + lrow, (int64_t)a.M - 1);  // rows past M: any valid row, discarded below
+      const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);  // rows past M: any valid row, discarded below
       q_rows[j] = (const uint16_t*)ga.hidden + (m * hc + h) * (int64_t)d + cw;
       kk[j] = qq[j] = kq[j] = 0.f;
     }
-    // per token: sums over this lane's 16 runs of 4 channels
+    // per token: sums over this lane's runs of 4 channels
 #pragma unroll
     for (int i = 0; i < TN; i++)
 #pragma unroll
@@ -317,21 +335,29 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_bf16(GemmGateArgs ga) {
       qq[j] += __shfl_xor(qq[j], 32, 64);
       kq[j] += __shfl_xor(kq[j], 32, 64);
     }
-    // the two waves of a token row (wn = 0, 1) meet in LDS; the operand stages are free now
+    // the WN waves of a token row meet in LDS; the operand stages are free now
     __syncthreads();
-    float4* red = reinterpret_cast<float4*>(&sA[0][0]);   // [wm][j][lrow] of wave wn = 1
-    if (wn == 1 && lhalf == 0)
+    float4* red = reinterpret_cast<float4*>(&sA[0][0]);   // [wn][wm][j][lrow]
+    if (lhalf == 0)
 #pragma unroll
-      for (int j = 0; j < TM; j++) red[(wm * TM + j) * 32 + lrow] = make_float4(kk[j], qq[j], kq[j], 0.f);
+      for (int j = 0; j < TM; j++)
+        red[((wn * WM + wm) * TM + j) * 32 + lrow] = make_float4(kk[j], qq[j], kq[j], 0.f);
     __syncthreads();
     if (wn == 0 && lhalf == 0) {
       const int n_part = d / BN, part = c0 / BN;
 #pragma unroll
       for (int j = 0; j < TM; j++) {
-        const int64_t m = m0 + wm * (BM / 2) + j * 32 + lrow;
+        const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
         if (m >= a.M) continue;
-        const float4 o = red[(wm * TM + j) * 32 + lrow];
-        ga.partials[(m * hc + h) * n_part + part] = make_float4(kk[j] + o.x, qq[j] + o.y, kq[j] + o.z, 0.f);
+        float4 o = red[(wm * TM + j) * 32 + lrow];
+#pragma unroll
+        for (int w2 = 1; w2 < WN; w2++) {
+          const float4 t = red[((w2 * WM + wm) * TM + j) * 32 + lrow];
+          o.x += t.x;
+          o.y += t.y;
+          o.z += t.z;
+        }
+        ga.partials[(m * hc + h) * n_part + part] = o;
       }
     }
   }
@@ -399,14 +425,16 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
 
 }  // namespace
 
-template <int BM, int BN, bool GATE>
+template <int BM, int BN, int WM, int WN, bool GATE>
 hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
-  k_gemm_bf16<BM, BN, GATE><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+  k_gemm_bf16<BM, BN, WM, WN, GATE><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
   return hipGetLastError();
 }
 
-// the largest tile that still gives every CU a few workgroups
+// Tile choice (measured on MI355X over the workloads' shapes): 256x256 with
+// 4x2 waves (2 per SIMD) once there are at least 4 such tiles per CU, else
+// 128x128 with 2x2 waves, whose 64 KB of LDS lets two workgroups share a CU.
 static int pick_tile_n(int64_t M, int N) {
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   return big >= 4 * 256 ? 256 : 128;
@@ -416,10 +444,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   GemmGateArgs ga = {};
   ga.g = a;
-  const int64_t mid = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
-  if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, false>(ga, s);
-  if (mid >= 2 * 256) return gemm_launch<256, 128, false>(ga, s);
-  return gemm_launch<128, 128, false>(ga, s);
+  if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, 4, 2, false>(ga, s);
+  return gemm_launch<128, 128, 2, 2, false>(ga, s);
 }
 
 int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
@@ -431,8 +457,8 @@ int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
   if (a.g.M == 0 || a.g.N == 0) return hipSuccess;
   const int bn = gemm_gate_tile_n(a.g.M, a.g.N, a.g.K, a.d);
-  if (bn == 256) return gemm_launch<256, 256, true>(a, s);
-  if (bn == 128) return gemm_launch<256, 128, true>(a, s);
+  if (bn == 256) return gemm_launch<256, 256, 4, 2, true>(a, s);
+  if (bn == 128) return gemm_launch<128, 128, 2, 2, true>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -244,6 +244,33 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }(std::make_integer_sequence<int, KK>{});
   };
 
+  // Fused gate, small wave tiles: the wave's Q tile (TN*TM*16 values per lane)
+  // is loaded into registers before the first operand loads, so it arrives
+  // under the K loop instead of in the epilogue.  (The first step's vmcnt wait
+  // also covers these loads; they travel with the prologue's operand loads.)
+  constexpr bool kPreloadQ = GATE && TN * TM <= 4;
+  const bool key_tile = GATE && (int)(n0 / ga.d) < ga.hc;
+  const int gate_h = GATE ? (int)(n0 / ga.d) : 0;
+  const int gate_cw = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) + wn * (BN / WN) + 4 * lhalf : 0;  // + 32 i + 8 q
+  auto q_row = [&](int j) {
+    // rows past M: any valid row, its sums are discarded
+    const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);
+    return (const uint16_t*)ga.hidden + (m * ga.hc + gate_h) * (int64_t)ga.d + gate_cw;
+  };
+  uint2 qpre[kPreloadQ ? TN : 1][4][kPreloadQ ? TM : 1];
+  if constexpr (kPreloadQ) {
+    if (key_tile) {
+#pragma unroll
+      for (int j = 0; j < TM; j++) {
+        const uint16_t* qr = q_row(j);
+#pragma unroll
+        for (int i = 0; i < TN; i++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) qpre[i][q][j] = *(const uint2*)(qr + 32 * i + 8 * q);
+      }
+    }
+  }
+
   // prologue: steps 0 .. kStages-2 in flight
   auto issue_all = [&](auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
@@ -294,15 +321,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
     // key tile of branch h: channels c0 .. c0+BN-1 of the branch
     const int c0 = (int)(n0 - (int64_t)h * d);
-    const int cw = c0 + wn * (BN / WN) + 4 * lhalf;   // + 32 i + 8 q + e
-    const uint16_t* gk = (const uint16_t*)ga.gamma_k + (int64_t)h * d + cw;
-    const uint16_t* gq = (const uint16_t*)ga.gamma_q + (int64_t)h * d + cw;
+    const uint16_t* gk = (const uint16_t*)ga.gamma_k + (int64_t)h * d + gate_cw;
+    const uint16_t* gq = (const uint16_t*)ga.gamma_q + (int64_t)h * d + gate_cw;
     const uint16_t* q_rows[TM];
     float kk[TM], qq[TM], kq[TM];
 #pragma unroll
     for (int j = 0; j < TM; j++) {
-      const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);  // rows past M: any valid row, discarded below
-      q_rows[j] = (const uint16_t*)ga.hidden + (m * hc + h) * (int64_t)d + cw;
+      q_rows[j] = q_row(j);
       kk[j] = qq[j] = kq[j] = 0.f;
     }
     // per token: sums over this lane's runs of 4 channels
@@ -318,7 +343,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
         for (int j = 0; j < TM; j++) {
           float qv[4];
-          load4(q_rows[j] + 32 * i + 8 * q, qv);
+          if constexpr (kPreloadQ) {
+            const uint2 u = qpre[i][q][j];
+            qv[0] = __uint_as_float(u.x << 16);
+            qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+            qv[2] = __uint_as_float(u.y << 16);
+            qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+          } else {
+            load4(q_rows[j] + 32 * i + 8 * q, qv);
+          }
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const float k = acc[i][j][4 * q + e];

@@ -244,11 +244,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }(std::make_integer_sequence<int, KK>{});
   };
 
-  // Fused gate, small wave tiles: the wave's Q tile (TN*TM*16 values per lane)
-  // is loaded into registers before the first operand loads, so it arrives
-  // under the K loop instead of in the epilogue.  (The first step's vmcnt wait
-  // also covers these loads; they travel with the prologue's operand loads.)
-  constexpr bool kPreloadQ = GATE && TN * TM <= 4;
+  // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
+  // lane each, as many as fit in 32 VGPRs) are loaded into registers before the
+  // first operand loads, so they arrive under the K loop instead of in the
+  // epilogue.  (The first step's vmcnt wait also covers these loads; they
+  // travel with the prologue's operand loads.)
+  constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
+  constexpr bool kPreloadQ = PJ > 0;
   const bool key_tile = GATE && (int)(n0 / ga.d) < ga.hc;
   const int gate_h = GATE ? (int)(n0 / ga.d) : 0;
   const int gate_cw = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) + wn * (BN / WN) + 4 * lhalf : 0;  // + 32 i + 8 q
@@ -257,11 +259,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);
     return (const uint16_t*)ga.hidden + (m * ga.hc + gate_h) * (int64_t)ga.d + gate_cw;
   };
-  uint2 qpre[kPreloadQ ? TN : 1][4][kPreloadQ ? TM : 1];
+  uint2 qpre[kPreloadQ ? TN : 1][4][kPreloadQ ? PJ : 1];
   if constexpr (kPreloadQ) {
     if (key_tile) {
 #pragma unroll
-      for (int j = 0; j < TM; j++) {
+      for (int j = 0; j < PJ; j++) {
         const uint16_t* qr = q_row(j);
 #pragma unroll
         for (int i = 0; i < TN; i++)
@@ -343,8 +345,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
         for (int j = 0; j < TM; j++) {
           float qv[4];
-          if constexpr (kPreloadQ) {
-            const uint2 u = qpre[i][q][j];
+          if (j < PJ) {
+            const uint2 u = qpre[i][q][j < PJ ? j : 0];
             qv[0] = __uint_as_float(u.x << 16);
             qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
             qv[2] = __uint_as_float(u.y << 16);

@@ -133,10 +133,14 @@ __device__ __forceinline__ void unpack8(const u32x4& lo, const u32x4& hi, float 
   }
 }
 
+// Workgroup order: the channel block varies fastest, so the workgroups that
+// run together write whole output rows (all branches and channels of the
+// same positions) rather than one slice of many rows.
 template <bool BF16, int KS>
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int groups = a.d >> 3;
-  const int gx = blockIdx.y * 256 + threadIdx.x;
+  const int cblocks = (a.hc * groups + 255) / 256;
+  const int gx = (int)(blockIdx.x % cblocks) * 256 + threadIdx.x;
   if (gx >= a.hc * groups) return;
   const int h = gx / groups;
   const int c0 = (gx - h * groups) * 8;
@@ -144,7 +148,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int T = a.seqlen;
   const int run_len = D * kConvIters;
   const int runs = (T + run_len - 1) / run_len;
-  int y = blockIdx.x;
+  int y = (int)(blockIdx.x / cblocks);
   const int r = y % D;
   y /= D;
   const int run = y % runs;
@@ -310,7 +314,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
   const int lanes = a.hc * (a.d / 8);
   const int run_len = a.dil * kConvIters;
   const int runs = (a.seqlen + run_len - 1) / run_len;
-  dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil), (lanes + 255) / 256);
+  dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil * ((lanes + 255) / 256)));
   return a.bf16 ? conv_dispatch<true>(a, grid, s) : conv_dispatch<false>(a, grid, s);
 }
 

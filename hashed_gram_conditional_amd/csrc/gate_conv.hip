@@ -133,14 +133,24 @@ __device__ __forceinline__ void unpack8(const u32x4& lo, const u32x4& hi, float 
   }
 }
 
-// Workgroup order: the channel block varies fastest, so the workgroups that
-// run together write whole output rows (all branches and channels of the
-// same positions) rather than one slice of many rows.
+// Workgroup order: workgroups are dispatched round-robin over the 8 XCDs, so
+// workgroup b runs on XCD b % 8; each XCD is given a contiguous range of
+// logical workgroups, and within it the channel block varies fastest.  The
+// workgroups of one output row (every branch of the same positions) then run
+// together on one XCD and read the row's value slices from that XCD's L2
+// instead of once per branch from memory.
+__device__ __forceinline__ int xcd_contiguous(int bid, int total) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
 template <bool BF16, int KS>
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int groups = a.d >> 3;
   const int cblocks = (a.hc * groups + 255) / 256;
-  const int gx = (int)(blockIdx.x % cblocks) * 256 + threadIdx.x;
+  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int gx = (L % cblocks) * 256 + threadIdx.x;
   if (gx >= a.hc * groups) return;
   const int h = gx / groups;
   const int c0 = (gx - h * groups) * 8;
@@ -148,7 +158,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int T = a.seqlen;
   const int run_len = D * kConvIters;
   const int runs = (T + run_len - 1) / run_len;
-  int y = (int)(blockIdx.x / cblocks);
+  int y = L / cblocks;
   const int r = y % D;
   y /= D;
   const int run = y % runs;

@@ -25,7 +25,7 @@ _cases = {}
 
 
 def case(name, **over):
-    key = (name, tuple(sorted(over.items())))
+    key = (name, repr(sorted(over.items())))
     if key not in _cases:
         _cases[key] = Case(name, **over)
     return _cases[key]
@@ -219,6 +219,23 @@ def test_forward_within_tolerance(eg, name, n):
     ref = c.y_at(pos)
     err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], ref)
     assert err <= TOL[c.w.dtype], err
+
+
+@pytest.mark.parametrize("over,fused", [
+    (dict(batch=2, seqlen=100, hidden=200, hc_mult=3), False),   # d % 128 != 0: stored projections + gate kernel
+    (dict(batch=3, seqlen=77, hidden=256, hc_mult=2), True),     # fused GEMM with a ragged token count
+    (dict(batch=1, seqlen=300, hidden=384, hc_mult=1, orders=[2, 3, 4], conv_dilation=4), True),
+])
+def test_forward_paths_on_ragged_shapes(eg, over, fused):
+    c = case("b4_t1024", **over)
+    names = eg.kernel_names(c.cfg())
+    assert (names[1] == "project_gate_gemm") == fused, names
+    y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    sync()
+    N = c.B * c.T
+    pos = c.sample_positions(96, seed=8)
+    err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], c.y_at(pos))
+    assert err <= TOL["bf16"], err
 
 
 def test_forward_is_deterministic(eg):

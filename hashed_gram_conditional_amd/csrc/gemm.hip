@@ -137,13 +137,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   constexpr int QB = BN / (NW * kRowsPerDma);
   constexpr int kPerStep = QA + QB;
   constexpr int KK = BK / 16;                          // MFMA k slices per step
-  __shared__ u32x4 sA[kStages][BM * kPieces];          // e tiles
-  __shared__ u32x4 sB[kStages][BN * kPieces];          // weight tiles
+  // one LDS block of kStages stages, each an e tile then a weight tile; after
+  // the K loop it holds the output tile on its way to memory
+  constexpr int kStageElems = (BM + BN) * kPieces;
+  __shared__ u32x4 smem[kStages * kStageElems];
+  static_assert(BM * BN * 2 <= kStages * kStageElems * 16, "output tile fits in the operand stages");
   const GemmArgs& a = ga.g;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: DMA LDS addresses stay scalar
   const int wm = wave % WM, wn = wave / WM;
   const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
   int mt, nt;
@@ -169,10 +172,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     constexpr int S = decltype(stage_tag)::value;
     constexpr int X = decltype(x_tag)::value;
     if constexpr (X < QA)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(&sA[S][(X * NW + wave) * 64]), 16, voff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(&smem[S * kStageElems + (X * NW + wave) * 64]), 16, voff,
                                                X * NW * kRowsPerDma * row_bytes, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&sB[S][((X - QA) * NW + wave) * 64]), 16, voff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&smem[S * kStageElems + BM * kPieces + ((X - QA) * NW + wave) * 64]),
+                                               16, voff,
                                                (X - QA) * NW * kRowsPerDma * row_bytes, 0, 0);
   };
   auto step_voff = [&](int kt) {
@@ -204,12 +208,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
     for (int i = 0; i < TN; i++) {
       const int r = wn * (BN / WN) + i * 32 + lrow;
-      fa[i] = __builtin_bit_cast(bf16x8, sB[S][r * kPieces + swz(r, piece)]);
+      fa[i] = __builtin_bit_cast(bf16x8, smem[S * kStageElems + BM * kPieces + r * kPieces + swz(r, piece)]);
     }
 #pragma unroll
     for (int j = 0; j < TM; j++) {
       const int r = wm * (BM / WM) + j * 32 + lrow;
-      fb[j] = __builtin_bit_cast(bf16x8, sA[S][r * kPieces + swz(r, piece)]);
+      fb[j] = __builtin_bit_cast(bf16x8, smem[S * kStageElems + r * kPieces + swz(r, piece)]);
     }
   };
   auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
@@ -219,6 +223,57 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
       for (int j = 0; j < TM; j++)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
+  // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
+  // lane each, as many as fit in 32 VGPRs) are loaded into registers before the
+  // first operand loads, so they arrive under the K loop instead of in the
+  // epilogue.  (The first step's vmcnt wait also covers these loads; they
+  // travel with the prologue's operand loads.)
+  constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
+  constexpr bool kPreloadQ = PJ > 0;
+  // The remaining token blocks of the Q tile come through LDS: the last K
+  // step's refill (which would only write zeros) loads them instead, 16 bytes
+  // per lane and whole 256-byte row runs per 16 lanes, into the stage no wave
+  // reads any more; each wave gets a private region of kQRows rows x QP
+  // pieces, piece c of row r stored at piece c ^ (r % QP).
+  constexpr bool kQInLds = GATE && PJ < TM;
+  constexpr int QP = (BN / WN) / 8;           // 16-byte pieces of one wave's channel span
+  constexpr int kQRows = (TM - PJ) * 32;
+  constexpr int kQElems = kQRows * QP;        // u32x4 per wave region
+  constexpr int kQStage = (kStages + kStages - 2) % kStages;   // the stage the last step refills
+  static_assert(!kQInLds || (kQElems == kPerStep * 64 && NW * kQElems <= kStageElems), "Q regions fill one refill");
+  const bool key_tile = GATE && (int)(n0 / ga.d) < ga.hc;
+  const int gate_h = GATE ? (int)(n0 / ga.d) : 0;
+  const int gate_cw = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) + wn * (BN / WN) + 4 * lhalf : 0;  // + 32 i + 8 q
+  auto q_row = [&](int j) {
+    // rows past M: any valid row, its sums are discarded
+    const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);
+    return (const uint16_t*)ga.hidden + (m * ga.hc + gate_h) * (int64_t)ga.d + gate_cw;
+  };
+  const int gate_c0 = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) : 0;   // first channel of the tile in its branch
+  const __amdgpu_buffer_rsrc_t rQ = [&] {
+    // Q rows of the tile's tokens, branch gate_h; loads past the last token read zero
+    const int64_t rows = min((int64_t)BM, a.M - m0);
+    const int64_t bytes = kQInLds && key_tile ? (rows * ga.hc - gate_h) * (int64_t)ga.d * 2 : 0;
+    const uint16_t* base = (const uint16_t*)ga.hidden + (kQInLds && key_tile ? (m0 * ga.hc + gate_h) * (int64_t)ga.d : 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+  }();
+  auto issue_q_one = [&](auto x_tag) {
+    constexpr int X = decltype(x_tag)::value;
+    const int pi = X * 64 + lane;
+    const int r = pi / QP, c = (pi % QP) ^ (r % QP);
+    const int tok = wm * (BM / WM) + 32 * (PJ + r / 32) + r % 32;
+    const int voff = (tok * ga.hc * ga.d + gate_c0 + wn * (BN / WN) + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, LDS_PTR(&smem[kQStage * kStageElems + wave * kQElems + X * 64]), 16,
+                                             voff, 0, 0, 0);
+  };
+  auto issue_q_part = [&](auto part_tag) {
+    constexpr int P = decltype(part_tag)::value;
+    constexpr int lo = P * kPerStep / KK, hi = (P + 1) * kPerStep / KK;
+    [&]<int... X>(std::integer_sequence<int, X...>) {
+      (issue_q_one(std::integral_constant<int, lo + X>{}), ...);
+    }(std::make_integer_sequence<int, hi - lo>{});
+  };
+
   // One K step; sched_barrier keeps the scheduler from regrouping the reads
   // and loads of a slice with their uses.
   auto step = [&](auto stage_tag, int kt) {
@@ -228,13 +283,19 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kPerStep));
     __builtin_amdgcn_s_barrier();
     const int voff = step_voff(kt + kStages - 1);
+    const bool q_refill = kQInLds && S == kStages - 1 && key_tile && kt + 1 == nk_pad;
     bf16x8 fa[2][TN], fb[2][TM];
     load_frags(stage_tag, 0, fa[0], fb[0]);
     // the stage being refilled was read by every wave before the barrier
     auto slice = [&](auto part_tag) {
       constexpr int P = decltype(part_tag)::value;
       if constexpr (P + 1 < KK) load_frags(stage_tag, P + 1, fa[(P + 1) & 1], fb[(P + 1) & 1]);
-      issue_part(next, voff, part_tag);
+      if constexpr (kQInLds && S == kStages - 1) {
+        if (q_refill) issue_q_part(part_tag);
+        else issue_part(next, voff, part_tag);
+      } else {
+        issue_part(next, voff, part_tag);
+      }
       __builtin_amdgcn_sched_barrier(0);
       mfmas(fa[P & 1], fb[P & 1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -244,21 +305,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }(std::make_integer_sequence<int, KK>{});
   };
 
-  // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
-  // lane each, as many as fit in 32 VGPRs) are loaded into registers before the
-  // first operand loads, so they arrive under the K loop instead of in the
-  // epilogue.  (The first step's vmcnt wait also covers these loads; they
-  // travel with the prologue's operand loads.)
-  constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
-  constexpr bool kPreloadQ = PJ > 0;
-  const bool key_tile = GATE && (int)(n0 / ga.d) < ga.hc;
-  const int gate_h = GATE ? (int)(n0 / ga.d) : 0;
-  const int gate_cw = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) + wn * (BN / WN) + 4 * lhalf : 0;  // + 32 i + 8 q
-  auto q_row = [&](int j) {
-    // rows past M: any valid row, its sums are discarded
-    const int64_t m = min(m0 + wm * (BM / WM) + j * 32 + lrow, (int64_t)a.M - 1);
-    return (const uint16_t*)ga.hidden + (m * ga.hc + gate_h) * (int64_t)ga.d + gate_cw;
-  };
   uint2 qpre[kPreloadQ ? TN : 1][4][kPreloadQ ? PJ : 1];
   if constexpr (kPreloadQ) {
     if (key_tile) {
@@ -292,23 +338,34 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   // drain the trailing out-of-range loads before the workgroup's LDS is reused or released
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // plain store of a tile: 4 consecutive channels (8 bytes) per store
+  // Store of a tile through LDS: the accumulators go to an LDS copy of the
+  // bf16 tile (16-byte piece c of row r at piece c ^ (r % RP)), then each
+  // lane stores one 16-byte piece, so a wave writes whole rows.
   auto store_tile = [&](uint16_t* __restrict__ C, int64_t ldc, int64_t col0, int64_t ncols) {
+    constexpr int RP = BN / 8;        // 16-byte pieces per tile row
+    constexpr int RPI = 64 / RP;      // tile rows per wave instruction
+    uint16_t* t = reinterpret_cast<uint16_t*>(&smem[0]);
+    __syncthreads();                  // every wave is done with the operand stages
 #pragma unroll
     for (int j = 0; j < TM; j++) {
-      const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
-      if (m >= a.M) continue;
+      const int row = wm * (BM / WM) + j * 32 + lrow;
 #pragma unroll
-      for (int i = 0; i < TN; i++) {
+      for (int i = 0; i < TN; i++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const int64_t n = col0 + wn * (BN / WN) + i * 32 + 8 * q + 4 * lhalf;
-          if (n >= ncols) continue;
+          const int pc = (wn * (BN / WN) + i * 32 + 8 * q) / 8;
           const bf16x4 v = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1],
                             (__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
-          *(bf16x4*)(C + m * ldc + n) = v;
+          *(bf16x4*)(t + row * BN + (pc ^ (row % RP)) * 8 + 4 * lhalf) = v;
         }
-      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r0 = wave * RPI; r0 < BM; r0 += NW * RPI) {
+      const int row = r0 + lane / RP, pc = lane % RP;
+      const int64_t m = m0 + row, n = col0 + pc * 8;
+      const u32x4 v = *(const u32x4*)(t + row * BN + (pc ^ (row % RP)) * 8);
+      if (m < a.M && n < ncols) *(u32x4*)(C + m * ldc + n) = v;
     }
   };
 
@@ -351,6 +408,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
             qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
             qv[2] = __uint_as_float(u.y << 16);
             qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+          } else if constexpr (kQInLds) {
+            const int r = (j - PJ) * 32 + lrow;
+            const uint16_t* qs = reinterpret_cast<const uint16_t*>(&smem[kQStage * kStageElems + wave * kQElems]);
+            const uint2 u = *(const uint2*)(qs + r * QP * 8 + (((4 * i + q) ^ (r % QP)) * 8) + 4 * lhalf);
+            qv[0] = __uint_as_float(u.x << 16);
+            qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+            qv[2] = __uint_as_float(u.y << 16);
+            qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
           } else {
             load4(q_rows[j] + 32 * i + 8 * q, qv);
           }
@@ -372,7 +437,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
     // the WN waves of a token row meet in LDS; the operand stages are free now
     __syncthreads();
-    float4* red = reinterpret_cast<float4*>(&sA[0][0]);   // [wn][wm][j][lrow]
+    float4* red = reinterpret_cast<float4*>(&smem[0]);   // [wn][wm][j][lrow]
     if (lhalf == 0)
 #pragma unroll
       for (int j = 0; j < TM; j++)

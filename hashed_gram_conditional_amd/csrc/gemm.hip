@@ -235,12 +235,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   // per lane and whole 256-byte row runs per 16 lanes, into the stage no wave
   // reads any more; each wave gets a private region of kQRows rows x QP
   // pieces, piece c of row r stored at piece c ^ (r % QP).
-  constexpr bool kQInLds = GATE && PJ < TM;
   constexpr int QP = (BN / WN) / 8;           // 16-byte pieces of one wave's channel span
   constexpr int kQRows = (TM - PJ) * 32;
   constexpr int kQElems = kQRows * QP;        // u32x4 per wave region
   constexpr int kQStage = (kStages + kStages - 2) % kStages;   // the stage the last step refills
-  static_assert(!kQInLds || (kQElems == kPerStep * 64 && NW * kQElems <= kStageElems), "Q regions fill one refill");
+  // (taken when the regions are exactly one step's refill; otherwise those
+  // token blocks are read from memory in the epilogue)
+  constexpr bool kQInLds = GATE && PJ < TM && kQElems == kPerStep * 64 && NW * kQElems <= kStageElems;
   const bool key_tile = GATE && (int)(n0 / ga.d) < ga.hc;
   const int gate_h = GATE ? (int)(n0 / ga.d) : 0;
   const int gate_cw = GATE ? (int)(n0 - (int64_t)gate_h * ga.d) + wn * (BN / WN) + 4 * lhalf : 0;  // + 32 i + 8 q

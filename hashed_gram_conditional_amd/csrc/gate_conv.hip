@@ -100,7 +100,10 @@ __global__ void __launch_bounds__(256) k_gate(GateArgs a) {
   }
 }
 
-constexpr int kConvIters = 16;  // positions a thread walks (stride D)
+// Positions a thread walks (stride D): 16 for large calls, where fewer and
+// longer walks re-read less history; 8 for small ones (short prefill chunks,
+// decode), where more and shorter walks finish sooner (measured on MI355X).
+constexpr int conv_iters(int64_t n_tok) { return n_tok >= 16384 ? 16 : 8; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -145,7 +148,7 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int total) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-template <bool BF16, int KS>
+template <bool BF16, int KS, int kConvIters>
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int groups = a.d >> 3;
   const int cblocks = (a.hc * groups + 255) / 256;
@@ -290,17 +293,17 @@ __global__ void __launch_bounds__(256) k_advance(AdvanceArgs a) {
   if (threadIdx.x == 0) a.n_past[b] = past + T;
 }
 
-template <bool BF16>
+template <bool BF16, int IT>
 hipError_t conv_dispatch(const ConvArgs& a, dim3 grid, hipStream_t s) {
   switch (a.ksize) {
-    case 1: k_conv<BF16, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_conv<BF16, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_conv<BF16, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: k_conv<BF16, 4><<<grid, 256, 0, s>>>(a); break;
-    case 5: k_conv<BF16, 5><<<grid, 256, 0, s>>>(a); break;
-    case 6: k_conv<BF16, 6><<<grid, 256, 0, s>>>(a); break;
-    case 7: k_conv<BF16, 7><<<grid, 256, 0, s>>>(a); break;
-    case 8: k_conv<BF16, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_conv<BF16, 1, IT><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_conv<BF16, 2, IT><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_conv<BF16, 3, IT><<<grid, 256, 0, s>>>(a); break;
+    case 4: k_conv<BF16, 4, IT><<<grid, 256, 0, s>>>(a); break;
+    case 5: k_conv<BF16, 5, IT><<<grid, 256, 0, s>>>(a); break;
+    case 6: k_conv<BF16, 6, IT><<<grid, 256, 0, s>>>(a); break;
+    case 7: k_conv<BF16, 7, IT><<<grid, 256, 0, s>>>(a); break;
+    case 8: k_conv<BF16, 8, IT><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -322,10 +325,12 @@ hipError_t launch_gate(const GateArgs& a, hipStream_t s) {
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
   if ((int64_t)a.batch * a.seqlen == 0) return hipSuccess;
   const int lanes = a.hc * (a.d / 8);
-  const int run_len = a.dil * kConvIters;
+  const int it = conv_iters((int64_t)a.batch * a.seqlen);
+  const int run_len = a.dil * it;
   const int runs = (a.seqlen + run_len - 1) / run_len;
   dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil * ((lanes + 255) / 256)));
-  return a.bf16 ? conv_dispatch<true>(a, grid, s) : conv_dispatch<false>(a, grid, s);
+  if (it == 16) return a.bf16 ? conv_dispatch<true, 16>(a, grid, s) : conv_dispatch<false, 16>(a, grid, s);
+  return a.bf16 ? conv_dispatch<true, 8>(a, grid, s) : conv_dispatch<false, 8>(a, grid, s);
 }
 
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {

@@ -464,17 +464,23 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   }
 }
 
-// g from the fused GEMM's partial sums: one thread per (token, branch)
-__global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// g from the fused GEMM's partial sums: one thread per (token, branch); the
+// partials are read 8 at a time with independent loads.
+__global__ void __launch_bounds__(64) k_gate_finalize(GateFinalizeArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (i >= (int64_t)a.n_tok * a.hc) return;
   const float4* p = a.partials + i * a.n_part;
   float kk = 0.f, qq = 0.f, kq = 0.f;
-  for (int t = 0; t < a.n_part; t++) {
-    const float4 v = p[t];
-    kk += v.x;
-    qq += v.y;
-    kq += v.z;
+  for (int t0 = 0; t0 < a.n_part; t0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) v[t] = t0 + t < a.n_part ? p[t0 + t] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      kk += v[t].x;
+      qq += v[t].y;
+      kq += v[t].z;
+    }
   }
   const float inv_d = 1.f / (float)a.d;
   const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
@@ -566,7 +572,7 @@ hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
 hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_tok * a.hc;
   if (n == 0) return hipSuccess;
-  k_gate_finalize<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  k_gate_finalize<<<(unsigned)((n + 63) / 64), 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -3,7 +3,10 @@ oracle evaluated at chosen positions (rows and hidden states regenerated on
 the host only where those positions read them)."""
 from __future__ import annotations
 
+import concurrent.futures
 import functools
+import multiprocessing
+import os
 
 import numpy as np
 
@@ -22,8 +25,27 @@ def normwise(x, ref) -> float:
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
+def oracle_workers() -> int:
+    """Worker processes for the oracle: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+_WORKER_CASES: dict = {}
+
+
+def _y_at_chunk(args):
+    """Pool worker: the oracle outputs of one chunk of positions (each worker
+    process builds the case once, from the workload name and overrides)."""
+    name, over, pos = args
+    key = (name, repr(over))
+    if key not in _WORKER_CASES:
+        _WORKER_CASES[key] = Case(name, **dict(over))
+    return _WORKER_CASES[key].y_at(pos)
+
+
 class Case:
     def __init__(self, name: str, **over):
+        self.name, self.over = name, tuple(sorted(over.items()))
         w = S.WORKLOADS[name]
         self.w = w.replace(**over) if over else w
         self.inp = S.Inputs(self.w)
@@ -62,6 +84,19 @@ class Case:
         gk, gq, cw = self.small
         return self.orc.forward_at(self.inp.ids, self.inp.remap, self.inp.table_rows(rows), self.wkv, gk, gq, cw,
                                    hid, pos, table_keys=rows, hidden_keys=need)
+
+    def y_at_many(self, pos, chunk: int = 128) -> np.ndarray:
+        """y_at over many positions, in contiguous chunks spread over a pool of
+        fresh worker processes (spawned: they share nothing with this one)."""
+        pos = np.asarray(pos, dtype=np.int64)
+        n = oracle_workers()
+        if n == 1 or len(pos) <= chunk:
+            return self.y_at(pos)
+        parts = np.array_split(pos, max(n, -(-len(pos) // chunk)))
+        ctx = multiprocessing.get_context("spawn")
+        with concurrent.futures.ProcessPoolExecutor(n, mp_context=ctx) as ex:
+            out = list(ex.map(_y_at_chunk, [(self.name, self.over, p) for p in parts]))
+        return np.concatenate(out)
 
     def sample_positions(self, n: int, seed: int = 0, head: int = 16) -> np.ndarray:
         """The first `head` positions of sequence 0, the last of the last sequence,

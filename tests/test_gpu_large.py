@@ -45,16 +45,17 @@ def test_large_table_gather_is_bit_exact(eg, big):
     idx = eg.engram_hash(big.cfg(), big.params, big.dev["ids"])
     e = eg.engram_gather(big.cfg(), big.params, idx)
     torch.cuda.synchronize()
-    pos = big.sample_positions(512, seed=5)
-    got = storage_numpy(e).reshape(big.B * big.T, -1)[pos]
-    assert np.array_equal(got, big.e_at(pos))
+    # every position, in slices (the oracle regenerates only the rows each reads)
+    got = storage_numpy(e).reshape(big.B * big.T, -1)
+    for pos in np.array_split(np.arange(big.B * big.T), 8):
+        assert np.array_equal(got[pos], big.e_at(pos))
 
 
 def test_large_table_forward_within_tolerance(eg, big):
     y = eg.forward(big.cfg(), big.params, big.dev["ids"], big.dev["hidden"])
     torch.cuda.synchronize()
-    pos = big.sample_positions(24, seed=6, head=8)
-    ref = big.y_at(pos)
+    pos = big.sample_positions(1024, seed=6)
+    ref = big.y_at_many(pos)
     got = to_f64(y).reshape(big.B * big.T, big.w.hc_mult, big.w.hidden)[pos]
     assert normwise(got, ref) <= TOL["bf16"]
 

@@ -115,7 +115,7 @@ def test_gather_bit_exact(eg, name):
     e = eg.engram_gather(c.cfg(), c.params, idx)
     sync()
     N = c.B * c.T
-    pos = np.arange(N) if N <= 4096 else c.sample_positions(2048, seed=1)
+    pos = np.arange(N)           # every position
     got = storage_numpy(e).reshape(N, -1)[pos]
     assert np.array_equal(got, c.e_at(pos))
 
@@ -209,14 +209,16 @@ def test_gate_conv_with_oracle_kv(eg, dtype, strong):
 
 
 # ------------------------------------------------------------------ whole forward
-@pytest.mark.parametrize("name,n", [("tiny_fp32", None), ("b4_t1024", 160), ("b8_t4096", 48)])
+@pytest.mark.parametrize("name,n", [("tiny_fp32", None), ("b4_t1024", None), ("b8_t4096", 1024)])
 def test_forward_within_tolerance(eg, name, n):
+    """Every position of the small workloads; at B=8, T=4096 the first 16
+    positions (the pad and zero-history edge), the last one and 1024 seeded."""
     c = case(name)
     y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
     sync()
     N = c.B * c.T
     pos = np.arange(N) if n is None else c.sample_positions(n, seed=3)
-    ref = c.y_at(pos)
+    ref = c.y_at_many(pos)
     err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], ref)
     assert err <= TOL[c.w.dtype], err
 
@@ -233,8 +235,8 @@ def test_forward_paths_on_ragged_shapes(eg, over, fused):
     y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
     sync()
     N = c.B * c.T
-    pos = c.sample_positions(96, seed=8)
-    err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], c.y_at(pos))
+    pos = np.arange(N)
+    err = normwise(to_f64(y).reshape(N, c.w.hc_mult, c.w.hidden)[pos], c.y_at_many(pos))
     assert err <= TOL["bf16"], err
 
 
@@ -285,9 +287,10 @@ def test_chunked_prefill_matches_single_prefill(eg):
 
 
 def test_decode_matches_oracle(eg):
-    """Decode-shaped workload: prompt prefill, then single-token steps with state;
-    each step's output must equal the oracle's prefill over the whole sequence."""
-    c = case("decode_b256", decode_steps=64)
+    """Decode-shaped workload: prompt prefill, then 512 single-token steps with
+    state; for 8 seeded sequences every position's output must equal the
+    oracle's prefill over the whole sequence."""
+    c = case("decode_b256")
     w = c.w
     P = w.decode_prompt
     cfgp = c.cfg(c.B, P)
@@ -309,9 +312,8 @@ def test_decode_matches_oracle(eg):
     sync()
     assert normwise(to_f64(y), to_f64(whole)) <= 1e-2
     rng = np.random.default_rng(4)
-    b = rng.choice(c.B, size=8, replace=False)
-    t = np.concatenate([[0, P - 1, P], rng.choice(np.arange(P + 1, c.T), size=5, replace=False)])
-    pos = (b[:, None] * c.T + t[None, :]).ravel()
-    ref = c.y_at(pos)
+    b = np.sort(rng.choice(c.B, size=8, replace=False))
+    pos = (b[:, None] * c.T + np.arange(c.T)[None, :]).ravel()
+    ref = c.y_at_many(pos)
     got = to_f64(y).reshape(c.B * c.T, w.hc_mult, w.hidden)[pos]
     assert normwise(got, ref) <= TOL[w.dtype]

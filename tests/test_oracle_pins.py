@@ -522,3 +522,13 @@ def test_forward_rejects_bad_config(oracle_lib):
     o = mk(orders=(3, 2))
     with pytest.raises(orc.OracleError):
         o.hash(np.zeros((1, 8), np.int32))
+
+
+def test_oracle_pool_matches_serial():
+    """The process-pool evaluation used by the large parity tests returns the
+    serial oracle's values, bit for bit, in position order."""
+    from cases import Case
+
+    c = Case("tiny_fp32")
+    pos = np.arange(c.B * c.T)[::-1].copy()
+    assert np.array_equal(c.y_at_many(pos, chunk=8), c.y_at(pos))

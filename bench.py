@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    ap.add_argument("--zipf", type=float, default=None,
+                    help="override the workload's Zipf exponent of the token stream (0 = uniform tokens: the "
+                         "control without the cache reuse of frequent n-grams)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain float32 copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -208,6 +211,8 @@ def main():
     from engram_synth.device import device_inputs
 
     w = S.WORKLOADS[args.config]
+    if args.zipf is not None:
+        w = w.replace(zipf_a=args.zipf)
     if w.decode_prompt:
         return bench_decode(args, w)
     inp = S.Inputs(w)
@@ -291,7 +296,7 @@ def main():
         "metric": METRIC, "value": round(N / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "vocab": w.vocab,
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "vocab": w.vocab, "zipf_a": w.zipf_a,
                    "orders": w.orders, "heads_per_order": w.heads_per_order, "head_dim": w.head_dim,
                    "hidden": w.hidden, "hc_mult": w.hc_mult, "table_rows": w.table_rows,
                    "tokens_per_step": N, "parallelism": "single-gpu"},

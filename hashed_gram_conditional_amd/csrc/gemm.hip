@@ -224,12 +224,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
-  // lane each, as many as fit in 32 VGPRs) are loaded into registers before the
-  // first operand loads, so they arrive under the K loop instead of in the
-  // epilogue.  (The first step's vmcnt wait also covers these loads; they
-  // travel with the prologue's operand loads.)
+  // lane each) are loaded into registers before the first operand loads, so
+  // they arrive under the K loop instead of in the epilogue -- the first
+  // kPreI channel blocks of them, as many as the register budget left by the
+  // K loop holds without spilling (24 VGPRs with 8 waves, 32 with 4).  (The
+  // first step's vmcnt wait also covers these loads; they travel with the
+  // prologue's operand loads.)
   constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
   constexpr bool kPreloadQ = PJ > 0;
+  constexpr int kPreI = kPreloadQ ? ((NW >= 8 ? 24 : 32) / (8 * PJ) < TN ? (NW >= 8 ? 24 : 32) / (8 * PJ) : TN) : 1;
   // The remaining token blocks of the Q tile come through LDS: the last K
   // step's refill (which would only write zeros) loads them instead, 16 bytes
   // per lane and whole 256-byte row runs per 16 lanes, into the stage no wave
@@ -306,14 +309,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }(std::make_integer_sequence<int, KK>{});
   };
 
-  uint2 qpre[kPreloadQ ? TN : 1][4][kPreloadQ ? PJ : 1];
+  uint2 qpre[kPreI][4][kPreloadQ ? PJ : 1];
   if constexpr (kPreloadQ) {
     if (key_tile) {
 #pragma unroll
       for (int j = 0; j < PJ; j++) {
         const uint16_t* qr = q_row(j);
 #pragma unroll
-        for (int i = 0; i < TN; i++)
+        for (int i = 0; i < kPreI; i++)
 #pragma unroll
           for (int q = 0; q < 4; q++) qpre[i][q][j] = *(const uint2*)(qr + 32 * i + 8 * q);
       }
@@ -403,13 +406,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
         for (int j = 0; j < TM; j++) {
           float qv[4];
-          if (j < PJ) {
-            const uint2 u = qpre[i][q][j < PJ ? j : 0];
+          if (j < PJ && i < kPreI) {
+            const uint2 u = qpre[i < kPreI ? i : 0][q][j < PJ ? j : 0];
             qv[0] = __uint_as_float(u.x << 16);
             qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
             qv[2] = __uint_as_float(u.y << 16);
             qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
-          } else if constexpr (kQInLds) {
+          } else if (kQInLds && j >= PJ) {
             const int r = (j - PJ) * 32 + lrow;
             const uint16_t* qs = reinterpret_cast<const uint16_t*>(&smem[kQStage * kStageElems + wave * kQElems]);
             const uint2 u = *(const uint2*)(qs + r * QP * 8 + (((4 * i + q) ^ (r % QP)) * 8) + 4 * lhalf);

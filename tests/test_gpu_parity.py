@@ -317,3 +317,27 @@ def test_decode_matches_oracle(eg):
     ref = c.y_at_many(pos)
     got = to_f64(y).reshape(c.B * c.T, w.hc_mult, w.hidden)[pos]
     assert normwise(got, ref) <= TOL[w.dtype]
+
+
+def test_decode_state_copy_resumes(eg):
+    """Checkpoint and resume of the decode state: after k steps the state is
+    copied; the remaining steps run from the original and from the copy give
+    identical outputs and end at the same position."""
+    c = case("decode_b256")
+    P, k, n = c.w.decode_prompt, 5, 12
+    cfgp, cfg1 = c.cfg(c.B, P), c.cfg(c.B, 1)
+    ids, hid = c.dev["ids"], c.dev["hidden"]
+    steps_ids = ids[:, P:].t().contiguous()
+    steps_hid = hid[:, P:].transpose(0, 1).contiguous()
+    ws = eg.alloc_workspace(cfgp)
+    st = eg.State(cfg1, c.B)
+    eg.forward(cfgp, c.params, ids[:, :P].contiguous(), hid[:, :P].contiguous(), state=st, workspace=ws)
+    for s in range(k):
+        eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=st, workspace=ws)
+    copy = st.clone()
+    a = [eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=st, workspace=ws).clone() for s in range(k, n)]
+    b = [eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=copy, workspace=ws).clone() for s in range(k, n)]
+    sync()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    assert torch.equal(st.n_past, copy.n_past)
+    assert st.n_past.cpu().tolist() == [P + n] * c.B

@@ -35,12 +35,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef ENGRAM_GEMM_BK
 #define ENGRAM_GEMM_BK 64
 #endif
-#ifndef ENGRAM_GEMM_STAGES
-#define ENGRAM_GEMM_STAGES 2
-#endif
 constexpr int BK = ENGRAM_GEMM_BK;           // reduction step (bf16 elements)
 constexpr int kPieces = BK / 8;              // 16-byte pieces per LDS row
-constexpr int kStages = ENGRAM_GEMM_STAGES;  // LDS ring depth
 constexpr int kRowsPerDma = 64 / kPieces;    // rows one 1 KB DMA instruction fills
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -129,7 +125,7 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
 // square).  Value tiles are stored to v_out.  Writing K and reading it back
 // is the largest traffic of the unfused path.
-template <int BM, int BN, int WM, int WN, bool GATE>
+template <int BM, int BN, int WM, int WN, int kStages, bool GATE>
 __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) {
   constexpr int NW = WM * WN;                          // waves
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // MFMA tiles per wave along tokens / channels
@@ -535,27 +531,32 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, bool GATE>
+template <int BM, int BN, int WM, int WN, int ST, bool GATE>
 hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
-  k_gemm_bf16<BM, BN, WM, WN, GATE><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
+  k_gemm_bf16<BM, BN, WM, WN, ST, GATE><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // Tile choice (measured on MI355X over the workloads' shapes): 256x256 with
 // 4x2 waves (2 per SIMD) once there are at least 4 such tiles per CU, else
-// 128x128 with 2x2 waves, whose 64 KB of LDS lets two workgroups share a CU.
+// 128x128 with 2x2 waves, whose 64 KB of LDS (two stages) lets two workgroups
+// share a CU -- or, when there are no more tiles than CUs (decode-sized
+// token counts), four stages in 128 KB: one workgroup per CU either way, and
+// three K steps of loads in flight instead of one.
 static int pick_tile_n(int64_t M, int N) {
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   return big >= 4 * 256 ? 256 : 128;
 }
+static bool few_tiles(int64_t M, int N) { return ((M + 127) / 128) * ((N + 127) / 128) <= 256; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   GemmGateArgs ga = {};
   ga.g = a;
-  if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, 4, 2, false>(ga, s);
-  return gemm_launch<128, 128, 2, 2, false>(ga, s);
+  if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, 4, 2, 2, false>(ga, s);
+  if (few_tiles(a.M, a.N)) return gemm_launch<128, 128, 2, 2, 4, false>(ga, s);
+  return gemm_launch<128, 128, 2, 2, 2, false>(ga, s);
 }
 
 int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
@@ -567,8 +568,9 @@ int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
   if (a.g.M == 0 || a.g.N == 0) return hipSuccess;
   const int bn = gemm_gate_tile_n(a.g.M, a.g.N, a.g.K, a.d);
-  if (bn == 256) return gemm_launch<256, 256, 4, 2, true>(a, s);
-  if (bn == 128) return gemm_launch<128, 128, 2, 2, true>(a, s);
+  if (bn == 256) return gemm_launch<256, 256, 4, 2, 2, true>(a, s);
+  if (bn == 128 && few_tiles(a.g.M, a.g.N)) return gemm_launch<128, 128, 2, 2, 4, true>(a, s);
+  if (bn == 128) return gemm_launch<128, 128, 2, 2, 2, true>(a, s);
   return hipErrorInvalidValue;
 }
 

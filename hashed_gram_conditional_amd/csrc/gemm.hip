@@ -133,10 +133,30 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   constexpr int QB = BN / (NW * kRowsPerDma);
   constexpr int kPerStep = QA + QB;
   constexpr int KK = BK / 16;                          // MFMA k slices per step
+  // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
+  // lane each) are loaded into registers before the first operand loads, so
+  // they arrive under the K loop instead of in the epilogue -- the first
+  // kPreI channel blocks of them, as many as the register budget left by the
+  // K loop holds without spilling (24 VGPRs with 8 waves, 32 with 4).  (The
+  // first step's vmcnt wait also covers these loads; they travel with the
+  // prologue's operand loads.)
+  constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
+  constexpr bool kPreloadQ = PJ > 0;
+  constexpr int kPreI = kPreloadQ ? ((NW >= 8 ? 24 : 32) / (8 * PJ) < TN ? (NW >= 8 ? 24 : 32) / (8 * PJ) : TN) : 1;
   // one LDS block of kStages stages, each an e tile then a weight tile; after
-  // the K loop it holds the output tile on its way to memory
+  // the K loop it holds the output tile on its way to memory.  The fused gate
+  // adds, past the stages, the tile's gamma_k and gamma_q (1 KB each) and per
+  // wave the Q pieces that are neither preloaded into registers nor brought in
+  // by the last refill (token blocks j < PJ, channel blocks i >= kPreI); both
+  // are loaded by DMA before the first operand step and read in the epilogue.
   constexpr int kStageElems = (BM + BN) * kPieces;
-  __shared__ u32x4 smem[kStages * kStageElems];
+  constexpr int kGammaElems = GATE ? 128 : 0;
+  constexpr bool kQ4 = GATE && PJ > 0 && kPreI < TN;
+  constexpr int QP4 = (TN - kPreI) * 4;            // 16-byte pieces per row of those channel blocks
+  constexpr int kQ4Elems = kQ4 ? PJ * 32 * QP4 : 0;
+  static_assert(kQ4Elems % 64 == 0, "whole DMA instructions");
+  constexpr int kGammaBase = kStages * kStageElems, kQ4Base = kGammaBase + kGammaElems;
+  __shared__ u32x4 smem[kStages * kStageElems + kGammaElems + NW * kQ4Elems];
   static_assert(BM * BN * 2 <= kStages * kStageElems * 16, "output tile fits in the operand stages");
   const GemmArgs& a = ga.g;
 
@@ -219,16 +239,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
       for (int j = 0; j < TM; j++)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  // Fused gate: the first PJ token blocks of the wave's Q tile (TN*16 values per
-  // lane each) are loaded into registers before the first operand loads, so
-  // they arrive under the K loop instead of in the epilogue -- the first
-  // kPreI channel blocks of them, as many as the register budget left by the
-  // K loop holds without spilling (24 VGPRs with 8 waves, 32 with 4).  (The
-  // first step's vmcnt wait also covers these loads; they travel with the
-  // prologue's operand loads.)
-  constexpr int PJ = GATE ? (TM < 4 / TN ? TM : 4 / TN) : 0;
-  constexpr bool kPreloadQ = PJ > 0;
-  constexpr int kPreI = kPreloadQ ? ((NW >= 8 ? 24 : 32) / (8 * PJ) < TN ? (NW >= 8 ? 24 : 32) / (8 * PJ) : TN) : 1;
   // The remaining token blocks of the Q tile come through LDS: the last K
   // step's refill (which would only write zeros) loads them instead, 16 bytes
   // per lane and whole 256-byte row runs per 16 lanes, into the stage no wave
@@ -253,8 +263,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   const __amdgpu_buffer_rsrc_t rQ = [&] {
     // Q rows of the tile's tokens, branch gate_h; loads past the last token read zero
     const int64_t rows = min((int64_t)BM, a.M - m0);
-    const int64_t bytes = kQInLds && key_tile ? (rows * ga.hc - gate_h) * (int64_t)ga.d * 2 : 0;
-    const uint16_t* base = (const uint16_t*)ga.hidden + (kQInLds && key_tile ? (m0 * ga.hc + gate_h) * (int64_t)ga.d : 0);
+    const bool use = (kQInLds || kQ4) && key_tile;
+    const int64_t bytes = use ? (rows * ga.hc - gate_h) * (int64_t)ga.d * 2 : 0;
+    const uint16_t* base = (const uint16_t*)ga.hidden + (use ? (m0 * ga.hc + gate_h) * (int64_t)ga.d : 0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
   }();
   auto issue_q_one = [&](auto x_tag) {
@@ -319,6 +330,34 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
   }
 
+  if constexpr (GATE) {
+    // gamma_k and gamma_q of the tile's channels (value tiles: zeros)
+    if (wave == 0) {
+      const int64_t goff = key_tile ? (int64_t)gate_h * ga.d + gate_c0 : 0;
+      const int gbytes = key_tile ? BN * 2 : 0;
+      const int gv = lane < BN / 8 ? lane * 16 : kOutOfRange;
+      const __amdgpu_buffer_rsrc_t rgk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)ga.gamma_k + goff), (short)0, gbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rgq =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)ga.gamma_q + goff), (short)0, gbytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rgk, LDS_PTR(&smem[kGammaBase]), 16, gv, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rgq, LDS_PTR(&smem[kGammaBase + 64]), 16, gv, 0, 0, 0);
+    }
+  }
+  if constexpr (kQ4) {
+    // piece c of row r of this wave's region at piece c ^ ((r / 4) % QP4)
+    [&]<int... X>(std::integer_sequence<int, X...>) {
+      ([&] {
+        const int pi = X * 64 + lane;
+        const int r = pi / QP4, c = (pi % QP4) ^ ((r / 4) % QP4);
+        const int tok = wm * (BM / WM) + 32 * (r / 32) + r % 32;
+        const int voff = (tok * ga.hc * ga.d + gate_c0 + wn * (BN / WN) + kPreI * 32 + c * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, LDS_PTR(&smem[kQ4Base + wave * kQ4Elems + X * 64]), 16, voff,
+                                                 0, 0, 0);
+      }(), ...);
+    }(std::make_integer_sequence<int, kQ4Elems / 64>{});
+  }
+
   // prologue: steps 0 .. kStages-2 in flight
   auto issue_all = [&](auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
@@ -380,8 +419,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
     // key tile of branch h: channels c0 .. c0+BN-1 of the branch
     const int c0 = (int)(n0 - (int64_t)h * d);
-    const uint16_t* gk = (const uint16_t*)ga.gamma_k + (int64_t)h * d + gate_cw;
-    const uint16_t* gq = (const uint16_t*)ga.gamma_q + (int64_t)h * d + gate_cw;
+    const uint16_t* gks = reinterpret_cast<const uint16_t*>(&smem[kGammaBase]) + wn * (BN / WN) + 4 * lhalf;
+    const uint16_t* gqs = reinterpret_cast<const uint16_t*>(&smem[kGammaBase + 64]) + wn * (BN / WN) + 4 * lhalf;
     const uint16_t* q_rows[TM];
     float kk[TM], qq[TM], kq[TM];
 #pragma unroll
@@ -395,8 +434,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         float x[4], y[4], g[4];
-        load4(gk + 32 * i + 8 * q, x);
-        load4(gq + 32 * i + 8 * q, y);
+        load4(gks + 32 * i + 8 * q, x);
+        load4(gqs + 32 * i + 8 * q, y);
 #pragma unroll
         for (int e = 0; e < 4; e++) g[e] = x[e] * y[e];
 #pragma unroll
@@ -404,6 +443,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
           float qv[4];
           if (j < PJ && i < kPreI) {
             const uint2 u = qpre[i < kPreI ? i : 0][q][j < PJ ? j : 0];
+            qv[0] = __uint_as_float(u.x << 16);
+            qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+            qv[2] = __uint_as_float(u.y << 16);
+            qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+          } else if (kQ4 && j < PJ) {
+            const int r = j * 32 + lrow;
+            const uint16_t* qs = reinterpret_cast<const uint16_t*>(&smem[kQ4Base + wave * kQ4Elems]);
+            const uint2 u = *(const uint2*)(qs + (r * QP4 + (((i - kPreI) * 4 + q) ^ ((r / 4) % QP4))) * 8 + 4 * lhalf);
             qv[0] = __uint_as_float(u.x << 16);
             qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
             qv[2] = __uint_as_float(u.y << 16);

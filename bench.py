@@ -184,6 +184,137 @@ def bench_decode(args, w):
     print(json.dumps(res))
 
 
+def bench_offload(args, w):
+    """Tables in pinned host memory mapped into the device (walk-through 4.4:
+    the hash needs only the ids, so the rows are fetched while the layers before
+    the Engram layer run).  Per step, with L layers of a dense FFN (d -> 4d -> d,
+    bf16 matmuls) standing in for those layers:
+      resident:  FFN x L, then engram_forward with the tables in HBM;
+      offloaded: at the step start a side stream hashes the ids and gathers the
+                 rows from host memory; the main stream runs FFN x L, waits for
+                 the side stream, then engram_forward_gathered.
+    Two ways to bring the rows in:
+      zero-copy: a GPU gather reading the host table over the link (32
+                 workgroups); it holds those CUs while it waits on the link;
+      host+DMA:  the indices are copied to host memory, host threads copy the
+                 rows into pinned staging (engram_gather_host), the DMA
+                 engines copy them to HBM: no compute units taken.
+    Reports the step times and the loss of each offloaded flow, for several L."""
+    import torch
+
+    import engram_synth as S
+    import hashed_gram_conditional_amd as eg
+    from engram_synth.device import device_inputs
+
+    inp = S.Inputs(w)
+    torch.cuda.set_device(0)
+    d = device_inputs(inp)
+    cfg = eg.EngramConfig.make(**w.config_kwargs(inp))
+    p = eg.Params(remap=d["remap"], tables=d["tables"], w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                  conv_w=d["conv_w"])
+    t = d["tables"]
+    host = eg.alloc_mapped_host(t.numel() * t.element_size())
+    host.copy_from(t)
+    ph = eg.Params(remap=d["remap"], tables=host, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                   conv_w=d["conv_w"])
+    N = w.batch * w.seqlen
+    ws = eg.alloc_workspace(cfg)
+    out = torch.empty((w.batch, w.seqlen, w.hc_mult, w.hidden), dtype=d["hidden"].dtype, device="cuda")
+    idx = torch.empty((w.batch, w.seqlen, cfg.n_heads), dtype=torch.int32, device="cuda")
+    e = torch.empty((w.batch, w.seqlen, cfg.emb_dim), dtype=d["hidden"].dtype, device="cuda")
+    x = torch.randn(N, w.hidden, dtype=torch.bfloat16, device="cuda")
+    w1 = torch.randn(w.hidden, 4 * w.hidden, dtype=torch.bfloat16, device="cuda") * 0.02
+    w2 = torch.randn(4 * w.hidden, w.hidden, dtype=torch.bfloat16, device="cuda") * 0.02
+    h1 = torch.empty(N, 4 * w.hidden, dtype=torch.bfloat16, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    hip = Hip()
+
+    def ffn(layers):
+        for _ in range(layers):
+            torch.matmul(x, w1, out=h1)
+            torch.matmul(h1, w2, out=x)
+
+    def resident(layers):
+        ffn(layers)
+        eg.forward(cfg, p, d["ids"], d["hidden"], out=out, workspace=ws, stream=main)
+
+    def offloaded(layers):
+        side.wait_stream(main)                     # the ids are known at the step start
+        with torch.cuda.stream(side):
+            eg.engram_hash(cfg, ph, d["ids"], out=idx, stream=side)
+            eg.engram_gather(cfg, ph, idx, out=e, stream=side)
+        ffn(layers)
+        main.wait_stream(side)
+        eg.forward_gathered(cfg, ph, e, d["hidden"], out=out, workspace=ws, stream=main)
+
+    idx_h = torch.empty(idx.shape, dtype=torch.int32, pin_memory=True)
+    e_h = torch.empty(e.shape, dtype=e.dtype, pin_memory=True)
+    ev_idx = torch.cuda.Event()
+
+    def offloaded_dma(layers):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            eg.engram_hash(cfg, p, d["ids"], out=idx, stream=side)
+            idx_h.copy_(idx, non_blocking=True)
+            ev_idx.record(side)
+        ffn(layers)
+        ev_idx.synchronize()                       # the host waits for the indices only
+        eg.engram_gather_host(cfg, host, idx_h, e_h)
+        with torch.cuda.stream(side):
+            e.copy_(e_h, non_blocking=True)
+        main.wait_stream(side)
+        eg.forward_gathered(cfg, ph, e, d["hidden"], out=out, workspace=ws, stream=main)
+
+    def timed(fn, steps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    steps = max(args.steps // 4, 10)
+    # the two halves of the offloaded step alone: hash + gather from host vs from HBM
+    gather_host = timed(lambda: eg.engram_gather(cfg, ph, eg.engram_hash(cfg, ph, d["ids"], out=idx), out=e), steps)
+    gather_dev = timed(lambda: eg.engram_gather(cfg, p, eg.engram_hash(cfg, p, d["ids"], out=idx), out=e), steps)
+    idx_h.copy_(idx)
+    eg.engram_gather_host(cfg, host, idx_h, e_h)   # first touch of the pinned buffers
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eg.engram_gather_host(cfg, host, idx_h, e_h)
+    gather_cpu = (time.perf_counter() - t0) / steps * 1e6
+    h2d = timed(lambda: e.copy_(e_h, non_blocking=True), steps)
+    rows_bytes = N * cfg.emb_dim * t.element_size()
+    rows = []
+    for layers in (0, 1, 2, 4, 8):
+        # the GEMM-heavy steps run at a power-limited clock that drifts between
+        # runs: the variants are measured in turns, three times, and the median kept
+        runs = {"ffn": [], "r": [], "o": [], "od": []}
+        for _ in range(3):
+            runs["ffn"].append(timed(lambda: ffn(layers), steps) if layers else 0.0)
+            runs["r"].append(timed(lambda: resident(layers), steps))
+            runs["o"].append(timed(lambda: offloaded(layers), steps))
+            runs["od"].append(timed(lambda: offloaded_dma(layers), steps))
+        ffn_us, r, o, od = (sorted(runs[k])[1] for k in ("ffn", "r", "o", "od"))
+        rows.append({"ffn_layers": layers, "ffn_us": round(ffn_us, 1), "resident_us": round(r, 1),
+                     "zero_copy_us": round(o, 1), "zero_copy_loss": round(o / r - 1.0, 4),
+                     "host_dma_us": round(od, 1), "host_dma_loss": round(od / r - 1.0, 4)})
+    torch.cuda.synchronize()
+    host.free()
+    res = {
+        "mode": "offload", "workload": w.name, "tokens_per_step": N, "table_bytes": t.numel() * t.element_size(),
+        "host_tables": "pinned host memory, mapped, non-coherent (device may cache)",
+        "hash_gather_from_host_us": round(gather_host, 1), "hash_gather_from_hbm_us": round(gather_dev, 1),
+        "host_rows_GBps": round(rows_bytes / (gather_host * 1e-6) / 1e9, 1),
+        "host_threads_gather_us": round(gather_cpu, 1), "rows_h2d_copy_us": round(h2d, 1),
+        "steps": steps, "per_ffn_layers": rows,
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +327,8 @@ def main():
     ap.add_argument("--zipf", type=float, default=None,
                     help="override the workload's Zipf exponent of the token stream (0 = uniform tokens: the "
                          "control without the cache reuse of frequent n-grams)")
+    ap.add_argument("--offload", action="store_true",
+                    help="tables in host memory: measure the prefetch flow against HBM-resident tables")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain float32 copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -213,6 +346,8 @@ def main():
     w = S.WORKLOADS[args.config]
     if args.zipf is not None:
         w = w.replace(zipf_a=args.zipf)
+    if args.offload:
+        return bench_offload(args, w)
     if w.decode_prompt:
         return bench_decode(args, w)
     inp = S.Inputs(w)

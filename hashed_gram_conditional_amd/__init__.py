@@ -26,8 +26,8 @@ STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too s
 
 # every entry point the header declares, in its order
 ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_gather",
-                "engram_project", "engram_gate_conv", "engram_forward", "engram_forward_timed",
-                "engram_forward_kernel_name", "engram_status_string"]
+                "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward", "engram_forward_gathered",
+                "engram_forward_timed", "engram_forward_kernel_name", "engram_status_string"]
 
 
 class EngramError(RuntimeError):
@@ -125,26 +125,90 @@ def load():
         lib.engram_state_bytes_per_sequence.restype = ctypes.c_size_t
         lib.engram_hash.argtypes = [cfgp, prmp, P, stp, P, P]
         lib.engram_gather.argtypes = [cfgp, prmp, P, P, P]
+        lib.engram_gather_host.argtypes = [cfgp, P, P, P, ctypes.c_int32]
         lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
         lib.engram_gate_conv.argtypes = [cfgp, prmp, P, P, stp, P, P, P]
         lib.engram_forward.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P]
+        lib.engram_forward_gathered.argtypes = [cfgp, prmp, P, P, P, stp, P, P, ctypes.c_size_t, P]
         lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_int32)]
         lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32]
         lib.engram_forward_kernel_name.restype = ctypes.c_char_p
         lib.engram_status_string.argtypes = [I]
         lib.engram_status_string.restype = ctypes.c_char_p
-        for f in ("engram_hash", "engram_gather", "engram_project", "engram_gate_conv", "engram_forward",
-                  "engram_forward_timed"):
+        for f in ("engram_hash", "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
+                  "engram_forward_gathered", "engram_forward_timed"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
 
 
 # ------------------------------------------------------------------ marshalling
+class MappedHost:
+    """Pinned host memory mapped into the device (e.g. host-resident tables):
+    `address` is the device-side address kernels use, from
+    hipHostGetDevicePointer.  Allocate with alloc_mapped_host."""
+
+    def __init__(self, address: int, host: int, nbytes: int):
+        self.address, self.host, self.nbytes = address, host, nbytes
+
+    def copy_from(self, t):
+        """Copy a contiguous device tensor's bytes into the start of this buffer."""
+        import torch
+
+        n = t.numel() * t.element_size()
+        if n > self.nbytes or not t.is_contiguous():
+            raise ValueError("tensor does not fit or is not contiguous")
+        torch.cuda.synchronize()
+        if _hip().hipMemcpy(ctypes.c_void_p(self.host), ctypes.c_void_p(t.data_ptr()), ctypes.c_size_t(n), 4) != 0:
+            raise RuntimeError("hipMemcpy failed")
+
+    def free(self):
+        if self.host:
+            _hip().hipHostFree(ctypes.c_void_p(self.host))
+            self.host = self.address = 0
+
+
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime already loaded by torch and by the library."""
+    global _hip_rt
+    if _hip_rt is None:
+        _hip_rt = ctypes.CDLL("libamdhip64.so.7")
+        _hip_rt.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        _hip_rt.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+        _hip_rt.hipHostFree.argtypes = [ctypes.c_void_p]
+        _hip_rt.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    return _hip_rt
+
+
+HOST_MAPPED, HOST_COHERENT, HOST_NONCOHERENT = 0x2, 0x40000000, 0x80000000
+
+
+def alloc_mapped_host(nbytes: int, coherent: bool = False) -> MappedHost:
+    """Pinned host memory, mapped into the current device.  Non-coherent (the
+    default) lets the device cache what it reads, which read-only tables allow."""
+    import torch
+
+    torch.cuda.init()
+    h = ctypes.c_void_p()
+    flags = HOST_MAPPED | (HOST_COHERENT if coherent else HOST_NONCOHERENT)
+    if _hip().hipHostMalloc(ctypes.byref(h), ctypes.c_size_t(nbytes), flags) != 0 or not h.value:
+        raise MemoryError(f"hipHostMalloc of {nbytes} bytes failed")
+    d = ctypes.c_void_p()
+    if _hip().hipHostGetDevicePointer(ctypes.byref(d), h, 0) != 0:
+        _hip().hipHostFree(h)
+        raise RuntimeError("hipHostGetDevicePointer failed")
+    return MappedHost(d.value, h.value, nbytes)
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
+    if isinstance(t, MappedHost):
+        return t.address
     if not t.is_cuda:
         raise ValueError("engram arguments must be device tensors")
     if not t.is_contiguous():
@@ -231,6 +295,26 @@ def engram_gather(cfg: EngramConfig, p: Params, idx, out=None, stream=None):
     return out
 
 
+def _host_ptr(t) -> int:
+    """Address of host memory: a MappedHost buffer, a CPU tensor or a numpy array."""
+    if isinstance(t, MappedHost):
+        return t.host
+    if hasattr(t, "__array_interface__"):
+        return t.__array_interface__["data"][0]
+    if t.is_cuda or not t.is_contiguous():
+        raise ValueError("engram_gather_host takes contiguous host memory")
+    return t.data_ptr()
+
+
+def engram_gather_host(cfg: EngramConfig, tables, idx, out, n_threads: int = 0):
+    """Row lookup on the host (tables in host memory): out[n][h] = tables row
+    idx[n][h] of head h.  `idx` and `out` are host tensors (pinned, for the DMA
+    copies around it); synchronous."""
+    _check("engram_gather_host", load().engram_gather_host(ctypes.byref(cfg), _host_ptr(tables), _host_ptr(idx),
+                                                           _host_ptr(out), n_threads))
+    return out
+
+
 def engram_project(cfg: EngramConfig, p: Params, e, out=None, stream=None):
     import torch
 
@@ -290,6 +374,23 @@ def forward(cfg: EngramConfig, p: Params, ids, hidden, state: Optional[State] = 
                                       _ptr(workspace), workspace.numel(), _stream(stream), arr, len(events),
                                       ctypes.byref(nk))
         _check("engram_forward_timed", rc)
+    return out
+
+
+def forward_gathered(cfg: EngramConfig, p: Params, e, hidden, ids=None, state: Optional[State] = None, out=None,
+                     workspace=None, stream=None):
+    """Engram.forward on rows gathered beforehand (`e` [B][T][E] as written by
+    engram_gather); `ids` only when a state is advanced.  Returns out."""
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult, cfg.hidden), dtype=_real_dtype(cfg), device=e.device)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, e.device)
+    st = None if state is None else ctypes.byref(state._c)
+    rc = load().engram_forward_gathered(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(e), _ptr(hidden), st,
+                                        _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("engram_forward_gathered", rc)
     return out
 
 

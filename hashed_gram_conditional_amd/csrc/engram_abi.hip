@@ -1,8 +1,13 @@
 // Host side of the Engram C ABI (include/engram.h): argument validation, the
 // per-call hash constants, the workspace layout of engram_forward and the
-// order of kernel launches.  Allocates nothing and keeps no mutable state.
+// order of kernel launches; and the host-memory gather for tables kept in
+// host memory.  Allocates nothing and keeps no mutable state.
 #include <math.h>
 #include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
 
 #include "engram_internal.h"
 
@@ -47,6 +52,30 @@ engram_status check_params(const engram_config* c, const engram_params* p) {
     return ENGRAM_EINVAL;
   if (!aligned(p->tables, 16) || !aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) ||
       !aligned(p->conv_w, 4))
+    return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+// Grid cap of the gather when the tables are pinned host memory mapped into
+// the device: 32 workgroups keep ~1 MB of row loads in flight, enough for the
+// host link, and leave the other CUs to the work the prefetch overlaps.
+constexpr int kHostGatherBlocks = 32;
+
+int gather_grid_cap(const void* tables) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, tables) != hipSuccess) {
+    (void)hipGetLastError();   // not known to the runtime: treat as device memory, clear the error
+    return 0;
+  }
+  return at.type == hipMemoryTypeHost ? kHostGatherBlocks : 0;
+}
+
+// the same, for calls that do not read the tables
+engram_status check_params_no_tables(const engram_config* c, const engram_params* p) {
+  (void)c;
+  if (p == nullptr || p->w_kv == nullptr || p->gamma_k == nullptr || p->gamma_q == nullptr || p->conv_w == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) || !aligned(p->conv_w, 4))
     return ENGRAM_EINVAL;
   return ENGRAM_OK;
 }
@@ -208,17 +237,24 @@ struct Timer {
   }
 };
 
-engram_status forward_impl(const engram_config* c, const engram_params* p, const int32_t* ids, const void* hidden,
-                           engram_state* st, void* out, void* ws, size_t ws_bytes, hipStream_t s, hipEvent_t* ev,
-                           int32_t n_ev, int32_t* n_kernels) {
+// The forward pass.  gathered == false: the hash and gather run first (K1)
+// into the workspace.  gathered == true: e_in holds the rows already gathered
+// (the caller's prefetch) and K1 is skipped; the tables are not read, and ids
+// are needed only to advance a state.
+engram_status forward_impl(const engram_config* c, const engram_params* p, const int32_t* ids, bool gathered,
+                           const void* e_in, const void* hidden, engram_state* st, void* out, void* ws,
+                           size_t ws_bytes, hipStream_t s, hipEvent_t* ev, int32_t n_ev, int32_t* n_kernels) {
   engram_status rc = validate(c);
   if (rc) return rc;
-  if ((rc = check_params(c, p)) || (rc = check_state(c, st))) return rc;
+  if ((rc = gathered ? check_params_no_tables(c, p) : check_params(c, p))) return rc;
+  if ((rc = check_state(c, st))) return rc;
   const int64_t N = (int64_t)c->batch * c->seqlen;
-  const int nk = st ? 5 : 4;
+  const int nk = (st ? 5 : 4) - (gathered ? 1 : 0);
   if (n_kernels) *n_kernels = N == 0 ? 0 : nk;
   if (N == 0) return ENGRAM_OK;
-  if (ids == nullptr || hidden == nullptr || out == nullptr || ws == nullptr) return ENGRAM_EINVAL;
+  if ((!gathered || st != nullptr) && ids == nullptr) return ENGRAM_EINVAL;
+  if (gathered && (e_in == nullptr || !aligned(e_in, 16))) return ENGRAM_EINVAL;
+  if (hidden == nullptr || out == nullptr || ws == nullptr) return ENGRAM_EINVAL;
   if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(ws, 256)) return ENGRAM_EINVAL;
   const Workspace w = carve(c, ws);
   if (ws_bytes < w.bytes) return ENGRAM_ENOMEM;
@@ -229,15 +265,21 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   Timer tm{ev, n_ev, 0, s};
   hipError_t e;
 
-  GatherArgs ga = gather_args(c, p, ids, st);
-  ga.e_out = (uint8_t*)w.e;
-  if ((e = tm.before()) || (e = launch_hash_gather(hc, ga, true, s)) || (e = tm.after())) return hip_status(e);
+  const void* e_rows = e_in;
+  if (!gathered) {
+    GatherArgs ga = gather_args(c, p, ids, st);
+    ga.e_out = (uint8_t*)w.e;
+    const int cap = gather_grid_cap(p->tables);
+    if ((e = tm.before()) || (e = launch_hash_gather(hc, ga, true, s, cap)) || (e = tm.after()))
+      return hip_status(e);
+    e_rows = w.e;
+  }
 
   const void* v;
   int64_t v_stride;
   if (w.kv == nullptr) {  // fused: projections with the gate sums, then g
     GemmGateArgs gg;
-    gg.g = gemm_args(c, p, w.e, nullptr);
+    gg.g = gemm_args(c, p, e_rows, nullptr);
     gg.hidden = hidden;
     gg.gamma_k = p->gamma_k;
     gg.gamma_q = p->gamma_q;
@@ -260,7 +302,7 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
     v = w.v;
     v_stride = c->hidden;
   } else {
-    const GemmArgs gm = gemm_args(c, p, w.e, w.kv);
+    const GemmArgs gm = gemm_args(c, p, e_rows, w.kv);
     if ((e = tm.before()) || (e = bf16 ? launch_gemm_bf16(gm, s) : launch_gemm_f32(gm, s)) || (e = tm.after()))
       return hip_status(e);
     const GateArgs gt = gate_args(c, p, w.kv, hidden, w.g);
@@ -348,7 +390,7 @@ engram_status engram_gather(const engram_config* cfg, const engram_params* prm, 
   GatherArgs a = gather_args(cfg, prm, nullptr, nullptr);
   a.idx_in = idx;
   a.e_out = (uint8_t*)e_out;
-  return hip_status(launch_hash_gather(hc, a, false, stream));
+  return hip_status(launch_hash_gather(hc, a, false, stream, gather_grid_cap(prm->tables)));
 }
 
 engram_status engram_project(const engram_config* cfg, const engram_params* prm, const void* e, void* kv_out,
@@ -380,7 +422,15 @@ engram_status engram_gate_conv(const engram_config* cfg, const engram_params* pr
 engram_status engram_forward(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
                              const void* hidden, engram_state* st, void* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  return forward_impl(cfg, prm, ids, hidden, st, out, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+  return forward_impl(cfg, prm, ids, false, nullptr, hidden, st, out, workspace, workspace_bytes, stream, nullptr, 0,
+                      nullptr);
+}
+
+engram_status engram_forward_gathered(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                      const void* e, const void* hidden, engram_state* st, void* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(cfg, prm, ids, true, e, hidden, st, out, workspace, workspace_bytes, stream, nullptr, 0,
+                      nullptr);
 }
 
 engram_status engram_forward_timed(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
@@ -388,8 +438,61 @@ engram_status engram_forward_timed(const engram_config* cfg, const engram_params
                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int32_t n_events,
                                    int32_t* n_kernels) {
   if (events == nullptr && n_events != 0) return ENGRAM_EINVAL;
-  return forward_impl(cfg, prm, ids, hidden, st, out, workspace, workspace_bytes, stream, events, n_events,
-                      n_kernels);
+  return forward_impl(cfg, prm, ids, false, nullptr, hidden, st, out, workspace, workspace_bytes, stream, events,
+                      n_events, n_kernels);
+}
+
+engram_status engram_gather_host(const engram_config* cfg, const void* tables, const int32_t* idx, void* e_out,
+                                 int32_t n_threads) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  const int64_t N = (int64_t)cfg->batch * cfg->seqlen;
+  if (N == 0) return ENGRAM_OK;
+  if (tables == nullptr || idx == nullptr || e_out == nullptr) return ENGRAM_EINVAL;
+  const int H = n_heads(cfg);
+  const size_t row = (size_t)cfg->head_dim * esize(cfg);
+  int64_t off[ENGRAM_MAX_HEADS];
+  int64_t acc = 0;
+  for (int h = 0; h < H; h++) {
+    off[h] = acc;
+    acc += cfg->primes[h];
+  }
+  // row i = n*H + h of e_out is table row off[h] + idx[i] (clamped into [0, p_h) like engram_gather).
+  // The rows are scattered over the table, so each thread asks for the cache
+  // lines of the row kAhead places ahead before it copies the current one.
+  const uint8_t* t = (const uint8_t*)tables;
+  auto src = [&](int64_t i) {
+    const int h = (int)(i % H);
+    const int64_t r = std::min<int64_t>(std::max<int64_t>(idx[i], 0), (int64_t)cfg->primes[h] - 1);
+    return t + (off[h] + r) * (int64_t)row;
+  };
+  auto copy = [&](int64_t lo, int64_t hi) {
+    constexpr int kAhead = 16;
+    uint8_t* e = (uint8_t*)e_out;
+    auto prefetch = [&](int64_t i) {
+      const uint8_t* p = src(i);
+      for (size_t b = 0; b < row; b += 64) __builtin_prefetch(p + b, 0, 0);
+      __builtin_prefetch(p + row - 1, 0, 0);
+    };
+    for (int64_t i = lo; i < std::min(hi, lo + kAhead); i++) prefetch(i);
+    for (int64_t i = lo; i < hi; i++) {
+      if (i + kAhead < hi) prefetch(i + kAhead);
+      memcpy(e + i * row, src(i), row);
+    }
+  };
+  const int64_t rows = N * H;
+  int nt = n_threads > 0 ? n_threads : (int)std::thread::hardware_concurrency();
+  // at least 8192 rows per thread: starting a thread costs about as much as copying that many
+  nt = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)nt, 16, rows / 8192 + 1}));
+  if (nt == 1) {
+    copy(0, rows);
+    return ENGRAM_OK;
+  }
+  std::vector<std::thread> pool;
+  pool.reserve(nt);
+  for (int k = 0; k < nt; k++) pool.emplace_back(copy, rows * k / nt, rows * (k + 1) / nt);
+  for (auto& th : pool) th.join();
+  return ENGRAM_OK;
 }
 
 const char* engram_forward_kernel_name(const engram_config* cfg, int32_t i) {

@@ -59,7 +59,9 @@ struct GatherArgs {
   int32_t row_bytes;        // head_dim * element size
 };
 
-hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s);
+// max_blocks > 0 caps the grid (the workgroups then loop over the token tiles)
+hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
+                              int max_blocks = 0);
 
 // ------------------------------------------------------------------ GEMM
 // C[M][N] = A[M][K] * B[N][K]^T (both operands K-contiguous), fp32 accumulate.

@@ -15,6 +15,12 @@
 // 16-byte pieces: consecutive lanes take consecutive pieces of e_t, so a
 // 128-byte bf16 row is one 8-lane load and every store is coalesced, and each
 // lane keeps 8 independent row loads in flight before it stores.
+//
+// Tables in host memory (mapped into the device): each row load then waits on
+// the host link for microseconds, and a workgroup per 16 tokens would hold
+// every CU while it waits, starving whatever runs beside it.  The launch is
+// then a small grid whose workgroups loop over the token tiles; a few of them
+// keep enough loads in flight to fill the link.
 #include "engram_internal.h"
 
 namespace engram {
@@ -48,85 +54,92 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
   __shared__ int64_t s_row[kTokens * ENGRAM_MAX_HEADS];
 
   const int64_t N = (int64_t)a.batch * a.seqlen;
-  const int64_t n0 = (int64_t)blockIdx.x * kTokens;
-  const int ntok = (int)min((int64_t)kTokens, N - n0);
   const int H = hc.n_heads;
   const int tid = threadIdx.x;
+  const int64_t n_tiles = (N + kTokens - 1) / kTokens;
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int64_t n0 = tile * kTokens;
+    const int ntok = (int)min((int64_t)kTokens, N - n0);
 
-  if (compute_hash) {
-    const int W = hc.max_order - 1;
-    for (int i = tid; i < ntok + W; i += kThreads) {
-      const int64_t n = n0 - W + i;
-      int32_t x = hc.pad_id;
-      if (n >= 0) {
-        const int32_t id = a.ids[n];
-        if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
+    if (compute_hash) {
+      const int W = hc.max_order - 1;
+      for (int i = tid; i < ntok + W; i += kThreads) {
+        const int64_t n = n0 - W + i;
+        int32_t x = hc.pad_id;
+        if (n >= 0) {
+          const int32_t id = a.ids[n];
+          if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
+        }
+        s_x[i] = x;
       }
-      s_x[i] = x;
+      __syncthreads();
+      for (int pr = tid; pr < ntok * H; pr += kThreads) {
+        const int ti = pr / H, h = pr - ti * H;
+        const int64_t n = n0 + ti;
+        const int64_t b = n / a.seqlen;
+        const int32_t t = (int32_t)(n - b * a.seqlen);
+        const int order = hc.orders[h / hc.heads_per_order];
+        uint64_t mix = 0;
+        for (int k = 0; k < order; k++) {
+          int32_t tok;
+          if (t - k >= 0) {
+            tok = s_x[W + ti - k];
+          } else {
+            const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
+            tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
+          }
+          mix ^= (uint64_t)(int64_t)tok * hc.mult[k];
+        }
+        const uint32_t r = floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
+        if (a.idx_out) a.idx_out[n * H + h] = (int32_t)r;
+        s_row[ti * H + h] = hc.row_off[h] + r;
+      }
+    } else {
+      for (int pr = tid; pr < ntok * H; pr += kThreads) {
+        const int ti = pr / H, h = pr - ti * H;
+        int32_t r = a.idx_in[(n0 + ti) * H + h];
+        r = r < 0 ? 0 : (r >= (int32_t)hc.prime[h] ? (int32_t)hc.prime[h] - 1 : r);
+        s_row[ti * H + h] = hc.row_off[h] + r;
+      }
     }
     __syncthreads();
-    for (int pr = tid; pr < ntok * H; pr += kThreads) {
-      const int ti = pr / H, h = pr - ti * H;
-      const int64_t n = n0 + ti;
-      const int64_t b = n / a.seqlen;
-      const int32_t t = (int32_t)(n - b * a.seqlen);
-      const int order = hc.orders[h / hc.heads_per_order];
-      uint64_t mix = 0;
-      for (int k = 0; k < order; k++) {
-        int32_t tok;
-        if (t - k >= 0) {
-          tok = s_x[W + ti - k];
-        } else {
-          const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
-          tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
-        }
-        mix ^= (uint64_t)(int64_t)tok * hc.mult[k];
+    if (a.e_out != nullptr) {
+      const int cpr = a.row_bytes / (int)sizeof(Chunk);  // pieces per table row
+      const int cpt = H * cpr;                           // pieces per token
+      const int total = ntok * cpt;
+      const Chunk* __restrict__ tab = reinterpret_cast<const Chunk*>(a.tables);
+      Chunk* __restrict__ e = reinterpret_cast<Chunk*>(a.e_out) + n0 * cpt;
+      auto src = [&](int c) -> const Chunk* {
+        const int ti = c / cpt;
+        const int r = c - ti * cpt;
+        const int h = r / cpr;
+        const int col = r - h * cpr;
+        return tab + s_row[ti * H + h] * cpr + col;
+      };
+      int base = tid;
+      // full rounds: kUnroll independent row loads in flight per lane, then the stores
+      for (; base + (kUnroll - 1) * kThreads < total; base += kThreads * kUnroll) {
+        Chunk v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) v[u] = *src(base + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) e[base + u * kThreads] = v[u];
       }
-      const uint32_t r = floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
-      if (a.idx_out) a.idx_out[n * H + h] = (int32_t)r;
-      s_row[ti * H + h] = hc.row_off[h] + r;
+      for (int c = base; c < total; c += kThreads) e[c] = *src(c);
     }
-  } else {
-    for (int pr = tid; pr < ntok * H; pr += kThreads) {
-      const int ti = pr / H, h = pr - ti * H;
-      int32_t r = a.idx_in[(n0 + ti) * H + h];
-      r = r < 0 ? 0 : (r >= (int32_t)hc.prime[h] ? (int32_t)hc.prime[h] - 1 : r);
-      s_row[ti * H + h] = hc.row_off[h] + r;
-    }
+    __syncthreads();   // s_x and s_row are rewritten by the next tile
   }
-  __syncthreads();
-  if (a.e_out == nullptr) return;
-
-  const int cpr = a.row_bytes / (int)sizeof(Chunk);  // pieces per table row
-  const int cpt = H * cpr;                           // pieces per token
-  const int total = ntok * cpt;
-  const Chunk* __restrict__ tab = reinterpret_cast<const Chunk*>(a.tables);
-  Chunk* __restrict__ e = reinterpret_cast<Chunk*>(a.e_out) + n0 * cpt;
-  auto src = [&](int c) -> const Chunk* {
-    const int ti = c / cpt;
-    const int r = c - ti * cpt;
-    const int h = r / cpr;
-    const int col = r - h * cpr;
-    return tab + s_row[ti * H + h] * cpr + col;
-  };
-  int base = tid;
-  // full rounds: kUnroll independent row loads in flight per lane, then the stores
-  for (; base + (kUnroll - 1) * kThreads < total; base += kThreads * kUnroll) {
-    Chunk v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) v[u] = *src(base + u * kThreads);
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) e[base + u * kThreads] = v[u];
-  }
-  for (int c = base; c < total; c += kThreads) e[c] = *src(c);
 }
 
 }  // namespace
 
-hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s) {
+hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
+                              int max_blocks) {
   const int64_t N = (int64_t)a.batch * a.seqlen;
   if (N == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((N + kTokens - 1) / kTokens);
+  int64_t tiles = (N + kTokens - 1) / kTokens;
+  if (max_blocks > 0 && tiles > max_blocks) tiles = max_blocks;
+  const unsigned blocks = (unsigned)tiles;
   const int ch = compute_hash ? 1 : 0;
   if (a.row_bytes % 16 == 0)
     k_hash_gather<u32x4><<<blocks, kThreads, 0, s>>>(hc, a, ch);

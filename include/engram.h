@@ -85,7 +85,11 @@ typedef struct engram_config {
  * [sum_{h'<h} primes[h'], + primes[h]) of one stacked table. */
 typedef struct engram_params {
   const int32_t *remap;     /* [vocab] raw -> compressed id; NULL: ids are already compressed */
-  const void *tables;       /* [sum primes][head_dim] dtype */
+  const void *tables;       /* [sum primes][head_dim] dtype; device memory, or pinned host memory
+                               mapped into the device (hipHostMalloc, address from
+                               hipHostGetDevicePointer): rows are then read over the host link
+                               by a gather limited to 32 workgroups, so that work on other
+                               streams keeps the rest of the GPU */
   const void *w_kv;         /* [(hc_mult+1)*hidden][E] dtype: key rows of branch 0..hc-1, then value rows */
   const void *gamma_k;      /* [hc_mult][hidden] dtype, RMSNorm scale of the keys */
   const void *gamma_q;      /* [hc_mult][hidden] dtype, RMSNorm scale of the queries (hidden states) */
@@ -124,6 +128,16 @@ engram_status engram_hash(const engram_config *cfg, const engram_params *prm, co
 engram_status engram_gather(const engram_config *cfg, const engram_params *prm, const int32_t *idx,
                             void *e_out, hipStream_t stream);
 
+/* The same lookup on the host, for tables kept in host memory (walk-through
+ * 4.4, inference offload): e_out[n][h] = row idx[n][h] of head h's table, exact
+ * copies, idx clamped like engram_gather.  tables, idx and e_out are HOST
+ * pointers (e.g. pinned memory, idx copied back from engram_hash's output, e_out
+ * then copied to the device by the DMA engines, so the lookup takes no compute
+ * units from the GPU).  Runs on up to n_threads host threads (<= 0: the host's
+ * cores, at most 16) and returns when the rows are copied; makes no HIP call. */
+engram_status engram_gather_host(const engram_config *cfg, const void *tables, const int32_t *idx, void *e_out,
+                                 int32_t n_threads);
+
 /* Key and value projections (formula sheet 2.2 steps 1 and 3): kv_out[n] =
  * w_kv . e[n], i.e. [B][T][hc_mult+1][hidden] dtype with the keys of each
  * branch first and the shared value last.  bf16 uses MFMA with float32
@@ -150,6 +164,19 @@ engram_status engram_gate_conv(const engram_config *cfg, const engram_params *pr
 engram_status engram_forward(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
                              const void *hidden, engram_state *st, void *out, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* The module on rows gathered beforehand (walk-through 4.4, inference with the
+ * tables in host memory: the hash depends only on the token ids, so the rows a
+ * layer needs can be looked up and brought to the device while the layers
+ * before it run; e.g. engram_hash + engram_gather from host-resident tables on
+ * a side stream).  e: [B][T][E] dtype, as written by engram_gather, 16-byte
+ * aligned; the tables are not read (prm->tables may be NULL).  ids: needed only
+ * when st is not NULL (the state's token ring is advanced from them).  Otherwise
+ * as engram_forward, with the same workspace size; the caller orders the
+ * gather before this call (same stream, or an event). */
+engram_status engram_forward_gathered(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                      const void *e, const void *hidden, engram_state *st, void *out,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Same as engram_forward, additionally recording events[2i] / events[2i+1]
  * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,

@@ -114,3 +114,54 @@ def test_status_strings_and_kernel_names(eg):
     assert lib.engram_status_string(-2) == b"workspace too small"
     assert eg.kernel_names(good(eg), with_state=True) == ["hash_gather", "project_gemm", "gate", "short_conv",
                                                          "advance_state"]
+
+
+def test_forward_gathered_validates_on_the_host(eg):
+    """engram_forward_gathered: the rows must be given (16-byte aligned); the
+    tables and (without a state) the ids are not needed.  A short workspace is
+    reported only once everything else passed, so -2 shows the rest was accepted."""
+    c = good(eg)
+    lib = eg.load()
+    P = ctypes.c_void_p
+    ws = eg.workspace_size(c)
+    no_tables = eg._Params(P(16), None, P(16), P(16), P(16), P(16))
+    f = lib.engram_forward_gathered
+    assert f(ctypes.byref(c), ctypes.byref(no_tables), None, P(16), P(16), None, P(16), P(256), ws - 1, None) == -2
+    assert f(ctypes.byref(c), ctypes.byref(no_tables), None, None, P(16), None, P(16), P(256), ws, None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(no_tables), None, P(24), P(16), None, P(16), P(256), ws, None) == -1
+    no_w = eg._Params(P(16), P(16), None, P(16), P(16), P(16))
+    assert f(ctypes.byref(c), ctypes.byref(no_w), None, P(16), P(16), None, P(16), P(256), ws, None) == -1
+    empty = good(eg, batch=0)
+    assert f(ctypes.byref(empty), ctypes.byref(no_tables), None, None, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("name,over", [("tiny_fp32", {}),
+                                       ("b4_t1024", dict(batch=2, seqlen=300, prime_base=4001))])
+def test_host_gather_matches_oracle(eg, name, over):
+    """engram_gather_host (host memory, no GPU): every gathered row equals the
+    oracle's, bit for bit, on 1 and on several threads; indices out of range
+    are clamped like the device gather."""
+    import numpy as np
+
+    from cases import Case
+
+    c = Case(name, **over)
+    cfg = c.cfg()
+    N = c.B * c.T
+    table = np.ascontiguousarray(c.inp.table())
+    idx = np.ascontiguousarray(c.idx.astype(np.int32))
+    ref = c.e_at(np.arange(N)).reshape(N, -1)
+    for threads in (1, 3, 0):
+        out = np.zeros_like(ref)
+        eg.engram_gather_host(cfg, table, idx, out, n_threads=threads)
+        assert np.array_equal(out, ref)
+    bad = idx.copy()
+    bad.reshape(-1)[:5] = [-1, 2**30, -5, 2**31 - 1, 0]
+    out = np.zeros_like(ref)
+    eg.engram_gather_host(cfg, table, bad, out)
+    H = idx.shape[-1]
+    p = np.asarray(c.inp.primes, dtype=np.int64)
+    clamped = np.clip(bad.reshape(N, H).astype(np.int64), 0, p[None, :] - 1)
+    off = np.concatenate([[0], np.cumsum(p)[:-1]])
+    rows = table.reshape(int(p.sum()), -1)[(clamped + off[None, :]).ravel()].reshape(N, -1)
+    assert np.array_equal(out, rows)

@@ -1,0 +1,112 @@
+"""Tables in host memory (architecture walk-through, yaoyuxiang.cn/news/830577,
+section 4.4, inference: the tables can live in host memory because the hash
+depends only on the token ids, so the rows a layer needs are known, and can be
+fetched, before the layer runs).
+
+The tables go to pinned host memory mapped into the device; the gather then
+reads them over the host link.  Checked bit for bit against the same calls
+with the tables in HBM:
+  - the whole forward reading host-resident tables;
+  - the prefetch flow: hash + gather from host tables on a side stream, then
+    the forward on the gathered rows (engram_forward_gathered);
+  - the same flow across a chunked prefill and decode steps with a state.
+"""
+import pytest
+
+from cases import Case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def eg():
+    import hashed_gram_conditional_amd as m
+
+    m.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def c4():
+    return Case("b4_t1024")
+
+
+@pytest.fixture(scope="module")
+def host_params(eg, c4):
+    d = c4.dev
+    t = d["tables"]
+    host = eg.alloc_mapped_host(t.numel() * t.element_size())
+    host.copy_from(t)
+    p = eg.Params(remap=d["remap"], tables=host, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                  conv_w=d["conv_w"])
+    yield p
+    torch.cuda.synchronize()
+    host.free()
+
+
+def test_forward_with_host_tables_is_bit_equal(eg, c4, host_params):
+    d = c4.dev
+    y_dev = eg.forward(c4.cfg(), c4.params, d["ids"], d["hidden"])
+    y_host = eg.forward(c4.cfg(), host_params, d["ids"], d["hidden"])
+    torch.cuda.synchronize()
+    assert torch.equal(y_dev, y_host)
+
+
+def test_prefetch_then_gathered_forward_is_bit_equal(eg, c4, host_params):
+    d = c4.dev
+    cfg = c4.cfg()
+    y_dev = eg.forward(cfg, c4.params, d["ids"], d["hidden"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        idx = eg.engram_hash(cfg, host_params, d["ids"], stream=side)
+        e = eg.engram_gather(cfg, host_params, idx, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    no_tables = eg.Params(remap=d["remap"], tables=None, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                          conv_w=d["conv_w"])
+    y = eg.forward_gathered(cfg, no_tables, e, d["hidden"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_dev)
+
+
+def test_prefetch_flow_with_state(eg, c4, host_params):
+    """Chunked prefill then single-token steps: hash (reading the state's token
+    history) and gather ahead, then the gathered forward advancing the state,
+    equal engram_forward with the same state sequence."""
+    d = c4.dev
+    B = c4.B
+    st_ref, st = eg.State(c4.cfg(), B), eg.State(c4.cfg(), B)
+    t0 = 0
+    for L in (300, 1, 1, 50, 1):
+        ids = d["ids"][:, t0:t0 + L].contiguous()
+        hid = d["hidden"][:, t0:t0 + L].contiguous()
+        cfg = c4.cfg(B, L)
+        ref = eg.forward(cfg, c4.params, ids, hid, state=st_ref)
+        idx = eg.engram_hash(cfg, host_params, ids, state=st)
+        e = eg.engram_gather(cfg, host_params, idx)
+        y = eg.forward_gathered(cfg, host_params, e, hid, ids=ids, state=st)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), (t0, L)
+        t0 += L
+    assert torch.equal(st.n_past, st_ref.n_past)
+    assert torch.equal(st.v_ring, st_ref.v_ring) and torch.equal(st.tok_ring, st_ref.tok_ring)
+
+
+def test_host_gather_and_dma_flow_is_bit_equal(eg, c4, host_params):
+    """The flow that keeps the lookup off the GPU's compute units: hash on the
+    GPU, indices copied to host memory, rows copied on the host
+    (engram_gather_host), rows copied to the device, gathered forward."""
+    d = c4.dev
+    cfg = c4.cfg()
+    y_dev = eg.forward(cfg, c4.params, d["ids"], d["hidden"])
+    idx = eg.engram_hash(cfg, c4.params, d["ids"])
+    idx_h = torch.empty(idx.shape, dtype=torch.int32, pin_memory=True)
+    idx_h.copy_(idx)
+    e_h = torch.empty((c4.B, c4.T, cfg.emb_dim), dtype=torch.bfloat16, pin_memory=True)
+    eg.engram_gather_host(cfg, host_params.tables, idx_h, e_h)
+    e = e_h.to("cuda", non_blocking=True)
+    y = eg.forward_gathered(cfg, host_params, e, d["hidden"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_dev)

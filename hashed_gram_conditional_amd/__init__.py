@@ -25,7 +25,8 @@ STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too s
           -3: "HIP launch or API call failed", -4: "configuration not supported by the kernels"}
 
 # every entry point the header declares, in its order
-ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_gather",
+ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_hash_layers",
+                "engram_gather",
                 "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward", "engram_forward_gathered",
                 "engram_forward_timed", "engram_forward_kernel_name", "engram_status_string"]
 
@@ -124,6 +125,7 @@ def load():
         lib.engram_state_bytes_per_sequence.argtypes = [cfgp]
         lib.engram_state_bytes_per_sequence.restype = ctypes.c_size_t
         lib.engram_hash.argtypes = [cfgp, prmp, P, stp, P, P]
+        lib.engram_hash_layers.argtypes = [cfgp, prmp, P, stp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P]
         lib.engram_gather.argtypes = [cfgp, prmp, P, P, P]
         lib.engram_gather_host.argtypes = [cfgp, P, P, P, ctypes.c_int32]
         lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
@@ -136,7 +138,7 @@ def load():
         lib.engram_forward_kernel_name.restype = ctypes.c_char_p
         lib.engram_status_string.argtypes = [I]
         lib.engram_status_string.restype = ctypes.c_char_p
-        for f in ("engram_hash", "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
+        for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
                   "engram_forward_gathered", "engram_forward_timed"):
             getattr(lib, f).restype = I
         _lib = lib
@@ -282,6 +284,25 @@ def engram_hash(cfg: EngramConfig, p: Params, ids, state: Optional[State] = None
     st = None if state is None else ctypes.byref(state._c)
     _check("engram_hash", load().engram_hash(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), st, _ptr(out),
                                              _stream(stream)))
+    return out
+
+
+def engram_hash_layers(cfg: EngramConfig, p: Params, ids, multipliers, state: Optional[State] = None, out=None,
+                       stream=None):
+    """Indices of several layers in one pass: `multipliers` is [L][<=8] ints
+    (layer l's m_k); returns int32 [L][B][T][H]."""
+    import torch
+
+    L = len(multipliers)
+    flat = (ctypes.c_int64 * (L * MAX_ORDERS))()
+    for l, ms in enumerate(multipliers):
+        for k, m in enumerate(ms):
+            flat[l * MAX_ORDERS + k] = ctypes.c_int64(int(m)).value
+    if out is None:
+        out = torch.empty((L, cfg.batch, cfg.seqlen, cfg.n_heads), dtype=torch.int32, device=ids.device)
+    st = None if state is None else ctypes.byref(state._c)
+    _check("engram_hash_layers", load().engram_hash_layers(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), st, flat,
+                                                           L, _ptr(out), _stream(stream)))
     return out
 
 

@@ -378,6 +378,34 @@ engram_status engram_hash(const engram_config* cfg, const engram_params* prm, co
   return hip_status(launch_hash_gather(hc, a, true, stream));
 }
 
+engram_status engram_hash_layers(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                 const engram_state* st, const int64_t* multipliers, int32_t n_layers,
+                                 int32_t* idx_out, hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if (prm == nullptr || multipliers == nullptr || n_layers < 1 || n_layers > ENGRAM_MAX_LAYERS) return ENGRAM_EINVAL;
+  if ((rc = check_state(cfg, st))) return rc;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (ids == nullptr || idx_out == nullptr) return ENGRAM_EINVAL;
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  LayerMults lm;
+  memset(&lm, 0, sizeof lm);
+  lm.n_layers = n_layers;
+  for (int l = 0; l < n_layers; l++)
+    for (int k = 0; k < ENGRAM_MAX_ORDERS; k++) lm.mult[l][k] = (uint64_t)multipliers[l * ENGRAM_MAX_ORDERS + k];
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  a.ids = ids;
+  a.remap = prm->remap;
+  a.idx_out = idx_out;
+  a.tok_ring = st ? st->tok_ring : nullptr;
+  a.n_past = st ? st->n_past : nullptr;
+  a.batch = cfg->batch;
+  a.seqlen = cfg->seqlen;
+  return hip_status(launch_hash_layers(hc, lm, a, stream));
+}
+
 engram_status engram_gather(const engram_config* cfg, const engram_params* prm, const int32_t* idx, void* e_out,
                             hipStream_t stream) {
   engram_status rc = validate(cfg);

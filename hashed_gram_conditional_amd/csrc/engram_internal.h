@@ -59,6 +59,14 @@ struct GatherArgs {
   int32_t row_bytes;        // head_dim * element size
 };
 
+// multipliers of several layers (layers share orders, heads and primes)
+struct LayerMults {
+  uint64_t mult[ENGRAM_MAX_LAYERS][ENGRAM_MAX_ORDERS];
+  int32_t n_layers;
+};
+// idx_out of a: [n_layers][N][H]
+hipError_t launch_hash_layers(const HashConsts& hc, const LayerMults& lm, const GatherArgs& a, hipStream_t s);
+
 // max_blocks > 0 caps the grid (the workgroups then loop over the token tiles)
 hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
                               int max_blocks = 0);

@@ -48,6 +48,47 @@ __device__ __forceinline__ uint32_t floored_mod(uint64_t u, uint32_t p, uint64_t
   return (uint32_t)r;
 }
 
+// Remapped ids of tokens n0-W .. n0+ntok-1 (W = max_order-1) into s_x; ids
+// before the start of the flattened batch read as pad.  Ends with a barrier.
+__device__ __forceinline__ void stage_window(const HashConsts& hc, const GatherArgs& a, int32_t* s_x, int64_t n0,
+                                             int ntok) {
+  const int W = hc.max_order - 1;
+  for (int i = threadIdx.x; i < ntok + W; i += kThreads) {
+    const int64_t n = n0 - W + i;
+    int32_t x = hc.pad_id;
+    if (n >= 0) {
+      const int32_t id = a.ids[n];
+      if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
+    }
+    s_x[i] = x;
+  }
+  __syncthreads();
+}
+
+// Hash of token n = n0 + ti for head h with multipliers mult: the mix over the
+// order's shifted tokens (from the staged window, or before position 0 of the
+// sequence from the state's token ring, else pad), then the floored mod.
+__device__ __forceinline__ uint32_t hash_one(const HashConsts& hc, const GatherArgs& a, const int32_t* s_x, int64_t n0,
+                                             int ti, int h, const uint64_t* mult) {
+  const int W = hc.max_order - 1;
+  const int64_t n = n0 + ti;
+  const int64_t b = n / a.seqlen;
+  const int32_t t = (int32_t)(n - b * a.seqlen);
+  const int order = hc.orders[h / hc.heads_per_order];
+  uint64_t mix = 0;
+  for (int k = 0; k < order; k++) {
+    int32_t tok;
+    if (t - k >= 0) {
+      tok = s_x[W + ti - k];
+    } else {
+      const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
+      tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
+    }
+    mix ^= (uint64_t)(int64_t)tok * mult[k];
+  }
+  return floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
+}
+
 template <typename Chunk>
 __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherArgs a, int compute_hash) {
   __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
@@ -62,36 +103,11 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
     const int ntok = (int)min((int64_t)kTokens, N - n0);
 
     if (compute_hash) {
-      const int W = hc.max_order - 1;
-      for (int i = tid; i < ntok + W; i += kThreads) {
-        const int64_t n = n0 - W + i;
-        int32_t x = hc.pad_id;
-        if (n >= 0) {
-          const int32_t id = a.ids[n];
-          if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
-        }
-        s_x[i] = x;
-      }
-      __syncthreads();
+      stage_window(hc, a, s_x, n0, ntok);
       for (int pr = tid; pr < ntok * H; pr += kThreads) {
         const int ti = pr / H, h = pr - ti * H;
-        const int64_t n = n0 + ti;
-        const int64_t b = n / a.seqlen;
-        const int32_t t = (int32_t)(n - b * a.seqlen);
-        const int order = hc.orders[h / hc.heads_per_order];
-        uint64_t mix = 0;
-        for (int k = 0; k < order; k++) {
-          int32_t tok;
-          if (t - k >= 0) {
-            tok = s_x[W + ti - k];
-          } else {
-            const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
-            tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
-          }
-          mix ^= (uint64_t)(int64_t)tok * hc.mult[k];
-        }
-        const uint32_t r = floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
-        if (a.idx_out) a.idx_out[n * H + h] = (int32_t)r;
+        const uint32_t r = hash_one(hc, a, s_x, n0, ti, h, hc.mult);
+        if (a.idx_out) a.idx_out[(n0 + ti) * H + h] = (int32_t)r;
         s_row[ti * H + h] = hc.row_off[h] + r;
       }
     } else {
@@ -131,7 +147,34 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
   }
 }
 
+// Indices of several layers in one pass: the window is staged once per tile and
+// each (token, head) is hashed with every layer's multipliers.
+__global__ void __launch_bounds__(kThreads) k_hash_layers(HashConsts hc, LayerMults lm, GatherArgs a) {
+  __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
+  const int64_t N = (int64_t)a.batch * a.seqlen;
+  const int H = hc.n_heads;
+  const int64_t n_tiles = (N + kTokens - 1) / kTokens;
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int64_t n0 = tile * kTokens;
+    const int ntok = (int)min((int64_t)kTokens, N - n0);
+    stage_window(hc, a, s_x, n0, ntok);
+    for (int pr = threadIdx.x; pr < ntok * H; pr += kThreads) {
+      const int ti = pr / H, h = pr - ti * H;
+      for (int l = 0; l < lm.n_layers; l++)
+        a.idx_out[((int64_t)l * N + n0 + ti) * H + h] = (int32_t)hash_one(hc, a, s_x, n0, ti, h, lm.mult[l]);
+    }
+    __syncthreads();   // s_x is rewritten by the next tile
+  }
+}
+
 }  // namespace
+
+hipError_t launch_hash_layers(const HashConsts& hc, const LayerMults& lm, const GatherArgs& a, hipStream_t s) {
+  const int64_t N = (int64_t)a.batch * a.seqlen;
+  if (N == 0) return hipSuccess;
+  k_hash_layers<<<(unsigned)((N + kTokens - 1) / kTokens), kThreads, 0, s>>>(hc, lm, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
                               int max_blocks) {

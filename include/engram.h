@@ -48,6 +48,7 @@ extern "C" {
 #define ENGRAM_MAX_HEADS 64
 #define ENGRAM_MAX_BRANCHES 16
 #define ENGRAM_MAX_CONV_KERNEL 8
+#define ENGRAM_MAX_LAYERS 16
 
 typedef enum {
   ENGRAM_OK = 0,
@@ -120,6 +121,18 @@ size_t engram_state_bytes_per_sequence(const engram_config *cfg);
  * read, not advanced.  idx_out: [B][T][H] int32, the row within head h's table. */
 engram_status engram_hash(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
                           const engram_state *st, int32_t *idx_out, hipStream_t stream);
+
+/* Hash indices of several Engram layers in one pass (formula sheet 1.4: each
+ * layer hashes with its own multipliers, seeded per layer; walk-through 4.3:
+ * one hash call gives every layer's indices, each layer takes its own).  The
+ * layers share cfg's orders, heads and primes; multipliers: HOST array
+ * [n_layers][ENGRAM_MAX_ORDERS] int64, layer l's m_k at [l][k] (cfg->multipliers
+ * is not used).  n_layers: 1..ENGRAM_MAX_LAYERS.  idx_out: [n_layers][B][T][H]
+ * int32, layer l's block equal to engram_hash with that layer's multipliers.
+ * ids and st as in engram_hash. */
+engram_status engram_hash_layers(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                 const engram_state *st, const int64_t *multipliers, int32_t n_layers,
+                                 int32_t *idx_out, hipStream_t stream);
 
 /* Multi-head embedding lookup and concatenation into e_t (walk-through 2.2-1
  * and 4.3).  idx: [B][T][H] as written by engram_hash; entries outside

@@ -165,3 +165,18 @@ def test_host_gather_matches_oracle(eg, name, over):
     off = np.concatenate([[0], np.cumsum(p)[:-1]])
     rows = table.reshape(int(p.sum()), -1)[(clamped + off[None, :]).ravel()].reshape(N, -1)
     assert np.array_equal(out, rows)
+
+
+def test_hash_layers_validates_on_the_host(eg):
+    c = good(eg)
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    mult = (ctypes.c_int64 * (16 * 8))(*range(1, 129))
+    f = lib.engram_hash_layers
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), None, mult, 0, P(16), None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), None, mult, 17, P(16), None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), None, None, 2, P(16), None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), None, None, mult, 2, P(16), None) == -1
+    empty = good(eg, batch=0)
+    assert f(ctypes.byref(empty), ctypes.byref(prm), None, None, mult, 2, None, None) == 0

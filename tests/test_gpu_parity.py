@@ -341,3 +341,45 @@ def test_decode_state_copy_resumes(eg):
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     assert torch.equal(st.n_past, copy.n_past)
     assert st.n_past.cpu().tolist() == [P + n] * c.B
+
+
+# ------------------------------------------------------------------ several layers
+def test_hash_layers_equal_single_layer_hashes(eg):
+    """One pass over three layers (each with its own multipliers) gives, for
+    every layer, the oracle's indices with that layer's multipliers; also
+    continuing a state."""
+    import dataclasses
+
+    import engram_synth as S
+    import oracle as orc
+
+    c = case("b4_t1024")
+    rng = np.random.default_rng(11)
+    mults = [S.make_multipliers(1002 + 7919 * l, c.w.max_order).tolist() for l in range(3)]
+    mults[2][0] = -(2**63) + 12345      # full int64 range, negative
+    got = eg.engram_hash_layers(c.cfg(), c.params, c.dev["ids"], mults)
+    sync()
+    for l in range(3):
+        o = orc.Oracle.from_workload(c.w, c.inp, batch=c.B, seqlen=c.T)
+        o.cfg.multipliers[:len(mults[l])] = mults[l]
+        ref = o.hash(c.inp.ids, remap=c.inp.remap)
+        assert np.array_equal(got[l].cpu().numpy(), ref), l
+    # continuing a state after a 100-token prefill
+    st = eg.State(c.cfg(), c.B)
+    eg.forward(c.cfg(c.B, 100), c.params, c.dev["ids"][:, :100].contiguous(), c.dev["hidden"][:, :100].contiguous(),
+               state=st)
+    ids2 = c.dev["ids"][:, 100:140].contiguous()
+    got2 = eg.engram_hash_layers(c.cfg(c.B, 40), c.params, ids2, mults, state=st)
+    for l in range(3):
+        cfg = c.cfg(c.B, 40)
+        for k in range(len(mults[l])):
+            cfg.multipliers[k] = ctypes_i64(mults[l][k])
+        one = eg.engram_hash(cfg, c.params, ids2, state=st)
+        sync()
+        assert torch.equal(got2[l], one), l
+
+
+def ctypes_i64(v):
+    import ctypes
+
+    return ctypes.c_int64(int(v)).value

@@ -76,8 +76,9 @@ def _load():
         lib.orc_conv.argtypes = [cp, P, P, P, P]
         lib.orc_forward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P]
         lib.orc_forward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, ctypes.c_int64, P, P]
+        lib.orc_backward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P, P, P, P, P, P, P]
         for f in ("orc_shift", "orc_hash", "orc_gather", "orc_project", "orc_gate", "orc_conv", "orc_forward",
-                  "orc_forward_at"):
+                  "orc_forward_at", "orc_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -249,6 +250,29 @@ class Oracle:
         trows, hrows = self._rows(table, tk), self._rows(hidden, hk)
         _ok(_load().orc_forward_at(ctypes.byref(c), _p(rm), len(rm), _p(ids), ctypes.byref(trows), *[_p(a) for a in args],
                                    ctypes.byref(hrows), len(pos), _p(pos), _p(out)), "orc_forward_at")
+        return out
+
+
+    def backward(self, ids, remap, table, w_kv, gamma_k, gamma_q, conv_w, hidden, dy) -> dict:
+        """Gradients of the module (orc_backward) for an upstream gradient dy
+        [B][T][hc][d]: dict of float64 arrays d_table [rows][Dh], d_w_kv,
+        d_gamma_k, d_gamma_q, d_conv_w, d_hidden (shapes of the inputs)."""
+        c = self.cfg
+        ids, rm = _c(ids, np.int32), _c(remap, np.int32)
+        table = _c(table, self.store)
+        args = [_c(a, self.store) for a in (w_kv, gamma_k, gamma_q, conv_w, hidden)]
+        dy = _c(dy, np.float64)
+        H, d, hc = self.n_heads, c.hidden, c.hc_mult
+        E = H * c.head_dim
+        rows = int(sum(int(c.primes[h]) for h in range(H)))
+        out = {"d_table": np.empty((rows, c.head_dim)), "d_w_kv": np.empty(((hc + 1) * d, E)),
+               "d_gamma_k": np.empty((hc, d)), "d_gamma_q": np.empty((hc, d)),
+               "d_conv_w": np.empty((hc, d, c.conv_kernel)), "d_hidden": np.empty((c.batch, c.seqlen, hc, d))}
+        trows = self._rows(table, None)
+        _ok(_load().orc_backward(ctypes.byref(c), _p(rm), len(rm), _p(ids), ctypes.byref(trows),
+                                 *[_p(a) for a in args], _p(dy),
+                                 *[_p(out[k]) for k in ("d_table", "d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w",
+                                                       "d_hidden")]), "orc_backward")
         return out
 
 

@@ -1,5 +1,5 @@
 /*
- * Engram conditional-memory forward pass: the ORACLE.
+ * Engram conditional-memory forward pass (and its gradients): the ORACLE.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, single-threaded
  * definition of what the forward pass computes, written from the two Engram
@@ -389,5 +389,143 @@ out1:
   free(e); free(q); free(kv); free(V); free(g);
 out0:
   free(idx); free(need);
+  return rc;
+}
+
+/* Gradients of the module's output (the backward pass of a training step;
+ * the pages train the module, walk-through 4.4).  Nothing here is on the
+ * pages: these are the exact derivatives of the forward definitions above,
+ * taken step by step backwards (chain rule), in double precision.  Given
+ * dy = dL/dy [B][T][hc][d] (double), with L a scalar loss of y:
+ *   conv + residual:  dVg[t] = dy[t] + sum_j w[j] dy[t + (K-1-j)D]  (inside the sequence)
+ *                     dw[h][c][j] = sum_t dy[t][h][c] Vg[t - (K-1-j)D][h][c]
+ *   value fusion:     dV[t][c] = sum_h g[t][h] dVg[t][h][c],  dg[t][h] = sum_c dVg[t][h][c] V[t][c]
+ *   gate:             da = dg g (1-g);  ds = da / (2 sqrt|s|) where |s| >= clamp and s != 0, else 0
+ *                     (a = sign(s) sqrt(max(|s|, clamp)) is flat in s inside the clamp)
+ *   s = sum_c u_c v_c / sqrt(d), u = K rk gk, v = Q rq gq:
+ *                     du = ds v / sqrt(d),  dv = ds u / sqrt(d)
+ *   RMSNorm:          dK_c = rk gk_c du_c - rk^3 K_c (sum_i du_i gk_i K_i) / d   (rk = (mean K^2 + eps)^-1/2)
+ *                     dgk_c += du_c K_c rk;  likewise dQ (= d hidden) and dgq
+ *   projections:      dW[o][i] = sum_t dKV[t][o] e[t][i],  de[t][i] = sum_o dKV[t][o] W[o][i]
+ *   gather:           dtable[row of (t, head)] += de[t][that head's slice]
+ * Outputs (all overwritten): d_table [sum p][Dh], d_w [(hc+1)d][E], d_gk and
+ * d_gq [hc][d], d_cw [hc][d][K], d_hidden [B][T][hc][d]. */
+int orc_backward(const orc_config *c, const int32_t *remap, int32_t vocab, const int32_t *ids, const orc_rows *table,
+                 const void *w_kv, const void *gamma_k, const void *gamma_q, const void *conv_w, const void *hidden,
+                 const double *dy, double *d_table, double *d_w, double *d_gk, double *d_gq, double *d_cw,
+                 double *d_hidden) {
+  if (check(c)) return ORC_EINVAL;
+  const int64_t T = c->seqlen, n = (int64_t)c->batch * T;
+  const int H = n_heads(c), hc = c->hc_mult, K = c->conv_kernel, D = c->conv_dilation;
+  const int64_t d = c->hidden, Dh = c->head_dim, E = (int64_t)H * Dh, O = (int64_t)(hc + 1) * d;
+  const int64_t esz = c->dtype == 0 ? 4 : 2;
+  int64_t rows = 0;
+  for (int h = 0; h < H; h++) rows += c->primes[h];
+  memset(d_table, 0, sizeof(double) * rows * Dh);
+  memset(d_w, 0, sizeof(double) * O * E);
+  memset(d_gk, 0, sizeof(double) * hc * d);
+  memset(d_gq, 0, sizeof(double) * hc * d);
+  memset(d_cw, 0, sizeof(double) * hc * d * K);
+  if (n == 0) return ORC_OK;
+
+  int64_t *idx = malloc(sizeof(int64_t) * n * H), off[ORC_MAX_HEADS];
+  void *e = malloc(esz * n * E);
+  double *kv = malloc(sizeof(double) * n * O), *s = malloc(sizeof(double) * n * hc);
+  double *g = malloc(sizeof(double) * n * hc), *dvg = malloc(sizeof(double) * n * hc * d);
+  double *dkv = malloc(sizeof(double) * n * O), *de = malloc(sizeof(double) * n * E);
+  int rc = ORC_ENOMEM;
+  if (!idx || !e || !kv || !s || !g || !dvg || !dkv || !de) goto out;
+  /* the forward quantities the derivatives use */
+  rc = orc_hash(c, remap, vocab, ids, NULL, idx);
+  if (!rc) rc = orc_gather(c, table, idx, n, e);
+  if (!rc) rc = orc_project(c, w_kv, e, n, kv);
+  if (!rc) rc = orc_gate(c, gamma_k, gamma_q, kv, hidden, n, s, g);
+  if (rc) goto out;
+  head_offsets(c, off);
+
+  /* conv + residual */
+  for (int64_t b = 0; b < c->batch; b++)
+    for (int64_t t = 0; t < T; t++)
+      for (int h = 0; h < hc; h++)
+        for (int64_t ch = 0; ch < d; ch++) {
+          const int64_t nn = b * T + t;
+          const double dyv = dy[(nn * hc + h) * d + ch];
+          double acc = dyv;
+          for (int j = 0; j < K; j++) {
+            const double w = ld(conv_w, ((int64_t)h * d + ch) * K + j, c->dtype);
+            const int64_t ahead = t + (int64_t)(K - 1 - j) * D, back = t - (int64_t)(K - 1 - j) * D;
+            if (ahead < T) acc += w * dy[((b * T + ahead) * hc + h) * d + ch];
+            if (back >= 0) {
+              const int64_t m = b * T + back;
+              d_cw[((int64_t)h * d + ch) * K + j] += dyv * g[m * hc + h] * kv[m * O + (int64_t)hc * d + ch];
+            }
+          }
+          dvg[(nn * hc + h) * d + ch] = acc;
+        }
+  /* value fusion and gate */
+  for (int64_t nn = 0; nn < n; nn++) {
+    for (int64_t ch = 0; ch < d; ch++) {
+      double acc = 0.0;
+      for (int h = 0; h < hc; h++) acc += g[nn * hc + h] * dvg[(nn * hc + h) * d + ch];
+      dkv[nn * O + (int64_t)hc * d + ch] = acc;
+    }
+    for (int h = 0; h < hc; h++) {
+      const double *Kv = kv + nn * O + (int64_t)h * d;
+      const int64_t q0 = (nn * hc + h) * d;
+      double dg = 0.0, kk = 0.0, qq = 0.0;
+      for (int64_t ch = 0; ch < d; ch++) {
+        const double q = ld(hidden, q0 + ch, c->dtype);
+        dg += dvg[q0 + ch] * kv[nn * O + (int64_t)hc * d + ch];
+        kk += Kv[ch] * Kv[ch];
+        qq += q * q;
+      }
+      const double gv = g[nn * hc + h], sv = s[nn * hc + h];
+      const double da = dg * gv * (1.0 - gv);
+      const double ds = (sv != 0.0 && fabs(sv) >= c->gate_clamp) ? da / (2.0 * sqrt(fabs(sv))) : 0.0;
+      const double rk = 1.0 / sqrt(kk / (double)d + c->norm_eps);
+      const double rq = 1.0 / sqrt(qq / (double)d + c->norm_eps);
+      const double sd = sqrt((double)d);
+      double A = 0.0, B = 0.0;
+      for (int64_t ch = 0; ch < d; ch++) {
+        const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
+        const double q = ld(hidden, q0 + ch, c->dtype);
+        const double u = Kv[ch] * rk * gk, v = q * rq * gq;
+        const double du = ds * v / sd, dv = ds * u / sd;
+        A += du * gk * Kv[ch];
+        B += dv * gq * q;
+        d_gk[(int64_t)h * d + ch] += du * Kv[ch] * rk;
+        d_gq[(int64_t)h * d + ch] += dv * q * rq;
+      }
+      for (int64_t ch = 0; ch < d; ch++) {
+        const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
+        const double q = ld(hidden, q0 + ch, c->dtype);
+        const double du = ds * q * rq * gq / sd, dv = ds * Kv[ch] * rk * gk / sd;
+        dkv[nn * O + (int64_t)h * d + ch] = rk * gk * du - rk * rk * rk * Kv[ch] * A / (double)d;
+        d_hidden[q0 + ch] = rq * gq * dv - rq * rq * rq * q * B / (double)d;
+      }
+    }
+  }
+  /* projections */
+  for (int64_t o = 0; o < O; o++)
+    for (int64_t i = 0; i < E; i++) {
+      double acc = 0.0;
+      for (int64_t nn = 0; nn < n; nn++) acc += dkv[nn * O + o] * ld(e, nn * E + i, c->dtype);
+      d_w[o * E + i] = acc;
+    }
+  for (int64_t nn = 0; nn < n; nn++)
+    for (int64_t i = 0; i < E; i++) {
+      double acc = 0.0;
+      for (int64_t o = 0; o < O; o++) acc += dkv[nn * O + o] * ld(w_kv, o * E + i, c->dtype);
+      de[nn * E + i] = acc;
+    }
+  /* gather */
+  for (int64_t nn = 0; nn < n; nn++)
+    for (int h = 0; h < H; h++) {
+      const int64_t r = off[h] + idx[nn * H + h];
+      for (int64_t j = 0; j < Dh; j++) d_table[r * Dh + j] += de[nn * E + (int64_t)h * Dh + j];
+    }
+  rc = ORC_OK;
+out:
+  free(idx); free(e); free(kv); free(s); free(g); free(dvg); free(dkv); free(de);
   return rc;
 }

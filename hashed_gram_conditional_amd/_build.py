@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libengram.so")
-SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gate_conv.hip"]
+SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gate_conv.hip", "backward.hip"]
 HEADERS = ["engram_internal.h", os.path.join("..", "..", "include", "engram.h")]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-shared", "-std=c++20", "-Wall",

@@ -155,6 +155,49 @@ Workspace carve(const engram_config* c, void* base) {
   return w;
 }
 
+// Workspace of engram_backward: the forward quantities it recomputes, the
+// gradients between steps, and the transposed GEMM operands (token axis
+// padded to a multiple of 64 with zeros).
+struct BwdWorkspace {
+  void* e;          // [N][E]
+  int32_t* idx;     // [N][H]
+  void* kv;         // [N][hc+1][d]
+  float4* stats;    // [N][hc] (g, s, rk, rq)
+  float* dvg;       // [N][hc][d]
+  void* dkv;        // [N][hc+1][d]
+  float* de;        // [N][E]
+  void* wT;         // [E][(hc+1)d]
+  void* dkvT;       // [(hc+1)d][Np]
+  void* eT;         // [E][Np]
+  int64_t Np;
+  size_t bytes;
+};
+
+BwdWorkspace carve_bwd(const engram_config* c, void* base) {
+  const int64_t N = (int64_t)c->batch * c->seqlen, E = emb_dim(c), O = (int64_t)(c->hc_mult + 1) * c->hidden;
+  const int64_t es = esize(c);
+  BwdWorkspace w = {};
+  w.Np = (N + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    void* p = (uint8_t*)base + off;
+    off += align_up(n);
+    return p;
+  };
+  w.e = take((size_t)(N * E * es));
+  w.idx = (int32_t*)take((size_t)N * n_heads(c) * sizeof(int32_t));
+  w.kv = take((size_t)(N * O * es));
+  w.stats = (float4*)take((size_t)N * c->hc_mult * sizeof(float4));
+  w.dvg = (float*)take((size_t)N * c->hc_mult * c->hidden * sizeof(float));
+  w.dkv = take((size_t)(N * O * es));
+  w.de = (float*)take((size_t)(N * E) * sizeof(float));
+  w.wT = take((size_t)(E * O * es));
+  w.dkvT = take((size_t)(O * w.Np * es));
+  w.eT = take((size_t)(E * w.Np * es));
+  w.bytes = off;
+  return w;
+}
+
 const char* const kForwardKernels[] = {"hash_gather", "project_gemm", "gate", "short_conv", "advance_state"};
 const char* const kFusedKernels[] = {"hash_gather", "project_gate_gemm", "gate_finalize", "short_conv",
                                      "advance_state"};
@@ -468,6 +511,106 @@ engram_status engram_forward_timed(const engram_config* cfg, const engram_params
   if (events == nullptr && n_events != 0) return ENGRAM_EINVAL;
   return forward_impl(cfg, prm, ids, false, nullptr, hidden, st, out, workspace, workspace_bytes, stream, events,
                       n_events, n_kernels);
+}
+
+size_t engram_backward_workspace_size(const engram_config* cfg) {
+  if (validate(cfg)) return 0;
+  return carve_bwd(cfg, nullptr).bytes;
+}
+
+engram_status engram_backward(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                              const void* hidden, const void* dy, void* d_hidden, float* d_tables, float* d_w_kv,
+                              float* d_gamma_k, float* d_gamma_q, float* d_conv_w, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if ((rc = check_params(cfg, prm))) return rc;
+  const int64_t N = (int64_t)cfg->batch * cfg->seqlen;
+  if (N == 0) return ENGRAM_OK;
+  if (ids == nullptr || hidden == nullptr || dy == nullptr || d_hidden == nullptr || d_tables == nullptr ||
+      d_w_kv == nullptr || d_gamma_k == nullptr || d_gamma_q == nullptr || d_conv_w == nullptr || workspace == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(dy, 16) || !aligned(d_hidden, 16) || !aligned(workspace, 256) ||
+      !aligned(d_tables, 4) || !aligned(d_w_kv, 4) || !aligned(d_gamma_k, 4) || !aligned(d_gamma_q, 4) ||
+      !aligned(d_conv_w, 4))
+    return ENGRAM_EINVAL;
+  const BwdWorkspace w = carve_bwd(cfg, workspace);
+  if (workspace_bytes < w.bytes) return ENGRAM_ENOMEM;
+  const bool bf16 = cfg->dtype == ENGRAM_BF16;
+  const int64_t E = emb_dim(cfg), O = (int64_t)(cfg->hc_mult + 1) * cfg->hidden;
+  const int es = (int)esize(cfg);
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  hipError_t e;
+  // forward quantities: rows, indices, projections, gate statistics
+  GatherArgs ga = gather_args(cfg, prm, ids, nullptr);
+  ga.idx_out = w.idx;
+  ga.e_out = (uint8_t*)w.e;
+  if ((e = launch_hash_gather(hc, ga, true, stream, gather_grid_cap(prm->tables)))) return hip_status(e);
+  const GemmArgs gm = gemm_args(cfg, prm, w.e, w.kv);
+  if ((e = bf16 ? launch_gemm_bf16(gm, stream) : launch_gemm_f32(gm, stream))) return hip_status(e);
+  GateArgs gt = gate_args(cfg, prm, w.kv, hidden, nullptr);
+  gt.stats = w.stats;
+  if ((e = launch_gate(gt, stream))) return hip_status(e);
+  // conv, gate, value fusion
+  ConvBwdArgs cb;
+  cb.dy = dy;
+  cb.kv = w.kv;
+  cb.stats = w.stats;
+  cb.conv_w = prm->conv_w;
+  cb.dvg = w.dvg;
+  cb.d_conv_w = d_conv_w;
+  cb.batch = cfg->batch;
+  cb.seqlen = cfg->seqlen;
+  cb.hc = cfg->hc_mult;
+  cb.d = cfg->hidden;
+  cb.ksize = cfg->conv_kernel;
+  cb.dil = cfg->conv_dilation;
+  cb.bf16 = bf16;
+  if ((e = launch_conv_bwd(cb, stream))) return hip_status(e);
+  GateBwdArgs gb;
+  gb.dvg = w.dvg;
+  gb.kv = w.kv;
+  gb.hidden = hidden;
+  gb.gamma_k = prm->gamma_k;
+  gb.gamma_q = prm->gamma_q;
+  gb.stats = w.stats;
+  gb.dkv = w.dkv;
+  gb.d_hidden = d_hidden;
+  gb.d_gamma_k = d_gamma_k;
+  gb.d_gamma_q = d_gamma_q;
+  gb.n_tok = (int32_t)N;
+  gb.hc = cfg->hc_mult;
+  gb.d = cfg->hidden;
+  gb.clamp = cfg->gate_clamp;
+  gb.inv_sqrt_d = (float)(1.0 / sqrt((double)cfg->hidden));
+  gb.bf16 = bf16;
+  if ((e = launch_gate_bwd(gb, stream))) return hip_status(e);
+  // de = dKV W (into float32), then the rows' gradients
+  if ((e = launch_transpose(prm->w_kv, w.wT, O, E, O, es, stream))) return hip_status(e);
+  GemmArgs g1;
+  g1.A = w.dkv;
+  g1.B = w.wT;
+  g1.C = w.de;
+  g1.M = (int32_t)N;
+  g1.N = (int32_t)E;
+  g1.K = (int32_t)O;
+  g1.accumulate = 0;
+  if ((e = bf16 ? launch_gemm_bf16_f32out(g1, stream) : launch_gemm_f32(g1, stream))) return hip_status(e);
+  if ((e = launch_scatter_add(hc, w.idx, w.de, d_tables, N, cfg->head_dim, stream))) return hip_status(e);
+  // dW += dKV^T e
+  if ((e = launch_transpose(w.dkv, w.dkvT, N, O, w.Np, es, stream))) return hip_status(e);
+  if ((e = launch_transpose(w.e, w.eT, N, E, w.Np, es, stream))) return hip_status(e);
+  GemmArgs g2;
+  g2.A = w.dkvT;
+  g2.B = w.eT;
+  g2.C = d_w_kv;
+  g2.M = (int32_t)O;
+  g2.N = (int32_t)E;
+  g2.K = (int32_t)w.Np;
+  g2.accumulate = 1;
+  if ((e = bf16 ? launch_gemm_bf16_f32out(g2, stream) : launch_gemm_f32(g2, stream))) return hip_status(e);
+  return ENGRAM_OK;
 }
 
 engram_status engram_gather_host(const engram_config* cfg, const void* tables, const int32_t* idx, void* e_out,

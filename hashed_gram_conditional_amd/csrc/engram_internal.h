@@ -78,9 +78,12 @@ struct GemmArgs {
   const void* B;   // w_kv [N][K]
   void* C;         // kv  [M][N]
   int32_t M, N, K;
+  int32_t accumulate = 0;   // float32 outputs: C += A B^T instead of C = A B^T
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// bf16 operands, float32 result stored or accumulated into C (a.accumulate)
+hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 // Projection GEMM with the gate reductions in its epilogue (bf16).  Key tiles
@@ -116,7 +119,8 @@ struct GateArgs {
   const void* hidden;    // [N][hc][d]
   const void* gamma_k;   // [hc][d]
   const void* gamma_q;   // [hc][d]
-  float* g_out;          // [N][hc]
+  float* g_out;          // [N][hc] or null
+  float4* stats = nullptr;   // [N][hc] (g, s, rk, rq) or null: what the backward pass needs
   int32_t n_tok, hc, d;
   float eps, clamp, inv_sqrt_d;
   bool bf16;
@@ -138,6 +142,46 @@ struct ConvArgs {
 };
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- backward
+// dVg = dy + (conv taps applied ahead in time) and the taps' gradient (added)
+struct ConvBwdArgs {
+  const void* dy;          // [N][hc][d]
+  const void* kv;          // [N][hc+1][d] (values in the last block)
+  const float4* stats;     // [N][hc] (g, s, rk, rq)
+  const void* conv_w;      // [hc][d][K]
+  float* dvg;              // [N][hc][d]
+  float* d_conv_w;         // [hc][d][K], added to
+  int32_t batch, seqlen, hc, d, ksize, dil;
+  bool bf16;
+};
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
+
+// gate and RMSNorm gradients (dK, d hidden, d gammas), and dV
+struct GateBwdArgs {
+  const float* dvg;        // [N][hc][d]
+  const void* kv;          // [N][hc+1][d]
+  const void* hidden;      // [N][hc][d]
+  const void* gamma_k;     // [hc][d]
+  const void* gamma_q;
+  const float4* stats;     // [N][hc]
+  void* dkv;               // [N][hc+1][d]: dK blocks and dV
+  void* d_hidden;          // [N][hc][d]
+  float* d_gamma_k;        // [hc][d], added to
+  float* d_gamma_q;
+  int32_t n_tok, hc, d;
+  float clamp, inv_sqrt_d;
+  bool bf16;
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < ld_dst (elements of esz bytes)
+hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, int64_t ld_dst, int esz,
+                            hipStream_t s);
+
+// d_tables[row_off[h] + idx[n][h]][j] += de[n][h*Dh + j]
+hipError_t launch_scatter_add(const HashConsts& hc, const int32_t* idx, const float* de, float* d_tables,
+                              int64_t n_tok, int32_t head_dim, hipStream_t s);
 
 struct AdvanceArgs {
   const int32_t* ids;     // [B][T] raw

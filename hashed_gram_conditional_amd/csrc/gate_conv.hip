@@ -96,7 +96,9 @@ __global__ void __launch_bounds__(256) k_gate(GateArgs a) {
     const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
     const float rq = 1.f / sqrtf(qq * inv_d + a.eps);
     const float s = kq * rk * rq * a.inv_sqrt_d;
-    a.g_out[n * a.hc + h] = gate_activation(s, a.clamp);
+    const float g = gate_activation(s, a.clamp);
+    if (a.g_out) a.g_out[n * a.hc + h] = g;
+    if (a.stats) a.stats[n * a.hc + h] = make_float4(g, s, rk, rq);
   }
 }
 

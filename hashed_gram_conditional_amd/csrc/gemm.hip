@@ -125,7 +125,7 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
 // square).  Value tiles are stored to v_out.  Writing K and reading it back
 // is the largest traffic of the unfused path.
-template <int BM, int BN, int WM, int WN, int kStages, bool GATE>
+template <int BM, int BN, int WM, int WN, int kStages, bool GATE, bool F32OUT = false>
 __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) {
   constexpr int NW = WM * WN;                          // waves
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // MFMA tiles per wave along tokens / channels
@@ -408,7 +408,27 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
   };
 
-  if constexpr (!GATE) {
+  if constexpr (F32OUT) {
+    // float32 result (gradients): 4 consecutive columns per lane, stored or added
+    float* __restrict__ C = (float*)a.C;
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+      const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int64_t n = n0 + wn * (BN / WN) + i * 32 + 8 * q + 4 * lhalf;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (n + e < a.N) {
+              float* c = C + m * a.N + n + e;
+              *c = a.accumulate ? *c + acc[i][j][4 * q + e] : acc[i][j][4 * q + e];
+            }
+        }
+    }
+  } else if constexpr (!GATE) {
     store_tile((uint16_t*)a.C, a.N, n0, a.N);
   } else {
     const int d = ga.d, hc = ga.hc;
@@ -571,17 +591,17 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
     if (m >= a.M) continue;
     for (int j = 0; j < 4; j++) {
       const int64_t n = n0 + tx * 4 + j;
-      if (n < a.N) C[m * a.N + n] = acc[i][j];
+      if (n < a.N) C[m * a.N + n] = a.accumulate ? C[m * a.N + n] + acc[i][j] : acc[i][j];
     }
   }
 }
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int ST, bool GATE>
+template <int BM, int BN, int WM, int WN, int ST, bool GATE, bool F32OUT = false>
 hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
-  k_gemm_bf16<BM, BN, WM, WN, ST, GATE><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
+  k_gemm_bf16<BM, BN, WM, WN, ST, GATE, F32OUT><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -604,6 +624,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, 4, 2, 2, false>(ga, s);
   if (few_tiles(a.M, a.N)) return gemm_launch<128, 128, 2, 2, 4, false>(ga, s);
   return gemm_launch<128, 128, 2, 2, 2, false>(ga, s);
+}
+
+hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  GemmGateArgs ga = {};
+  ga.g = a;
+  if (few_tiles(a.M, a.N)) return gemm_launch<128, 128, 2, 2, 4, false, true>(ga, s);
+  return gemm_launch<128, 128, 2, 2, 2, false, true>(ga, s);
 }
 
 int gemm_gate_tile_n(int64_t M, int N, int K, int d) {

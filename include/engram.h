@@ -191,6 +191,31 @@ engram_status engram_forward_gathered(const engram_config *cfg, const engram_par
                                       const void *e, const void *hidden, engram_state *st, void *out,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace engram_backward needs (0 when the configuration is invalid). */
+size_t engram_backward_workspace_size(const engram_config *cfg);
+
+/* Gradients of the module (the backward pass of a training step; the
+ * walk-through, 4.4, trains it): the exact derivatives of engram_forward
+ * without a state, for an upstream gradient dy = dL/dout.  The forward
+ * quantities are recomputed from the inputs (same arguments as
+ * engram_forward); nothing from a previous forward call is needed.
+ *   dy, d_hidden: [B][T][hc_mult][hidden] dtype; d_hidden is written.
+ *   d_tables [sum primes][head_dim], d_w_kv [(hc_mult+1)*hidden][E],
+ *   d_gamma_k, d_gamma_q [hc_mult][hidden], d_conv_w [hc_mult][hidden][conv_kernel]:
+ *   float32, ADDED to (zero them for plain gradients; only the table rows the
+ *   hashes select change).
+ * Sums across tokens (table rows, gammas, taps) use float32 atomics, so their
+ * last bits may differ between runs; the gradients must be device memory.
+ * workspace: device memory of at least engram_backward_workspace_size(cfg)
+ * bytes, 256-byte aligned.  ENGRAM_EINVAL for a NULL or misaligned pointer
+ * (hidden, dy, d_hidden 16-byte aligned), ENGRAM_ENOMEM for a short workspace,
+ * both before anything is launched.  The gate's slope 1/(2 sqrt|s|) makes the
+ * gradients through it as sensitive to rounding as the score s is close to 0. */
+engram_status engram_backward(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                              const void *hidden, const void *dy, void *d_hidden, float *d_tables, float *d_w_kv,
+                              float *d_gamma_k, float *d_gamma_q, float *d_conv_w, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Same as engram_forward, additionally recording events[2i] / events[2i+1]
  * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,
  * for i < n_events/2.  Returns the number of kernels in *n_kernels (nullable).

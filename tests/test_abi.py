@@ -180,3 +180,30 @@ def test_hash_layers_validates_on_the_host(eg):
     assert f(ctypes.byref(c), ctypes.byref(prm), None, None, mult, 2, P(16), None) == -1
     empty = good(eg, batch=0)
     assert f(ctypes.byref(empty), ctypes.byref(prm), None, None, mult, 2, None, None) == 0
+
+
+def test_backward_validates_on_the_host(eg):
+    """engram_backward: every gradient and input pointer is required (hidden,
+    dy, d hidden 16-byte aligned); a short workspace is reported only once
+    the rest passed; an empty batch succeeds with nothing launched."""
+    c = good(eg)
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    ws = lib.engram_backward_workspace_size(ctypes.byref(c))
+    N, E, O = 32, 64, 3 * 32
+    assert ws >= N * E * (2 + 4) + N * O * 2 * 2 + N * 2 * 16
+    assert lib.engram_backward_workspace_size(ctypes.byref(good(eg, hc_mult=0))) == 0
+    f = lib.engram_backward
+    ok = [P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16)]
+    assert f(ctypes.byref(c), ctypes.byref(prm), *ok, P(256), ws - 1, None) == -2
+    for i in range(len(ok)):
+        args = list(ok)
+        args[i] = None
+        assert f(ctypes.byref(c), ctypes.byref(prm), *args, P(256), ws, None) == -1, i
+    args = list(ok)
+    args[1] = P(24)
+    assert f(ctypes.byref(c), ctypes.byref(prm), *args, P(256), ws, None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), *ok, None, ws, None) == -1
+    empty = good(eg, batch=0)
+    assert f(ctypes.byref(empty), ctypes.byref(prm), *([None] * 9), None, 0, None) == 0

@@ -315,6 +315,82 @@ def bench_offload(args, w):
     print(json.dumps(res))
 
 
+def bench_train(args, w):
+    """One training step of the module (walk-through 4.4 trains the tables and
+    weights with the model): engram_forward_train, which keeps the forward
+    quantities in the backward workspace, then engram_backward_saved for a
+    fixed upstream gradient.  The float32 gradients accumulate across steps, as
+    over micro-batches; the optimiser's update is not part of the module.
+    Also times engram_forward (inference) and engram_backward (recomputing the
+    forward quantities), and gives the rate of the saved backward's GEMM flops
+    (dE = dKV.W and dW = dKV^T.E) against the bf16 MFMA peak."""
+    import torch
+
+    import engram_synth as S
+    import hashed_gram_conditional_amd as eg
+    from engram_synth.device import device_inputs
+
+    inp = S.Inputs(w)
+    torch.cuda.set_device(0)
+    d = device_inputs(inp)
+    cfg = eg.EngramConfig.make(**w.config_kwargs(inp))
+    p = eg.Params(remap=d["remap"], tables=d["tables"], w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                  conv_w=d["conv_w"])
+    N = w.batch * w.seqlen
+    ws = eg.alloc_workspace(cfg)
+    bws = eg.alloc_backward_workspace(cfg)
+    out = torch.empty_like(d["hidden"])
+    dy = torch.randn(d["hidden"].shape, dtype=torch.float32, device="cuda").to(d["hidden"].dtype)
+    d_hidden, grads = eg.backward(cfg, p, d["ids"], d["hidden"], dy, workspace=bws)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        eg.forward(cfg, p, d["ids"], d["hidden"], out=out, workspace=ws, stream=stream)
+
+    def fwd_train():
+        eg.forward_train(cfg, p, d["ids"], d["hidden"], bws, out=out, stream=stream)
+
+    def bwd_saved():
+        eg.backward_saved(cfg, p, d["hidden"], dy, bws, grads=grads, d_hidden=d_hidden, stream=stream)
+
+    def bwd():
+        eg.backward(cfg, p, d["ids"], d["hidden"], dy, grads=grads, d_hidden=d_hidden, workspace=bws, stream=stream)
+
+    def train():
+        fwd_train()
+        bwd_saved()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    train_ms = timed(train)
+    fwd_train_ms = timed(fwd_train)
+    bwd_saved_ms = train_ms - fwd_train_ms
+    fwd_ms = timed(fwd)
+    bwd_ms = timed(bwd)
+    flops = 2 * 2.0 * N * cfg.emb_dim * (w.hc_mult + 1) * w.hidden
+    tflops = flops / (bwd_saved_ms * 1e-3) / 1e12
+    res = {
+        "mode": "train", "metric": "Engram forward + backward tokens/sec at 1 MI355X",
+        "value": round(N / (train_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(train_ms, 4),
+        "forward_train_ms": round(fwd_train_ms, 4), "backward_saved_ms": round(bwd_saved_ms, 4),
+        "inference_forward_ms": round(fwd_ms, 4), "backward_recompute_ms": round(bwd_ms, 4),
+        "steps": args.steps, "warmup": args.warmup,
+        "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "tokens_per_step": N},
+        "backward_gemm_flops": flops, "backward_gemm_TFLOPs_over_backward_time": round(tflops, 1),
+        "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if w.dtype == "bf16" else None,
+        "workspace_bytes": {"forward": ws.numel(), "backward": bws.numel()},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +405,8 @@ def main():
                          "control without the cache reuse of frequent n-grams)")
     ap.add_argument("--offload", action="store_true",
                     help="tables in host memory: measure the prefetch flow against HBM-resident tables")
+    ap.add_argument("--train", action="store_true",
+                    help="forward + backward (gradients of the tables and weights) per step")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain float32 copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -348,6 +426,8 @@ def main():
         w = w.replace(zipf_a=args.zipf)
     if args.offload:
         return bench_offload(args, w)
+    if args.train:
+        return bench_train(args, w)
     if w.decode_prompt:
         return bench_decode(args, w)
     inp = S.Inputs(w)

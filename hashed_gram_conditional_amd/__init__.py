@@ -28,6 +28,7 @@ STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too s
 ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_hash_layers",
                 "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
                 "engram_forward_gathered", "engram_backward_workspace_size", "engram_backward",
+                "engram_forward_train", "engram_backward_saved",
                 "engram_forward_timed", "engram_forward_kernel_name", "engram_status_string"]
 
 
@@ -135,6 +136,8 @@ def load():
         lib.engram_backward_workspace_size.argtypes = [cfgp]
         lib.engram_backward_workspace_size.restype = ctypes.c_size_t
         lib.engram_backward.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.engram_forward_train.argtypes = [cfgp, prmp, P, P, P, P, ctypes.c_size_t, P]
+        lib.engram_backward_saved.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_int32)]
         lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32]
@@ -142,7 +145,8 @@ def load():
         lib.engram_status_string.argtypes = [I]
         lib.engram_status_string.restype = ctypes.c_char_p
         for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
-                  "engram_forward_gathered", "engram_backward", "engram_forward_timed"):
+                  "engram_forward_gathered", "engram_backward", "engram_forward_train", "engram_backward_saved",
+                  "engram_forward_timed"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -421,6 +425,26 @@ def forward_gathered(cfg: EngramConfig, p: Params, e, hidden, ids=None, state: O
 GRAD_NAMES = ("d_tables", "d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w")
 
 
+def backward_workspace_size(cfg: EngramConfig) -> int:
+    return load().engram_backward_workspace_size(ctypes.byref(cfg))
+
+
+def alloc_backward_workspace(cfg: EngramConfig, device="cuda"):
+    import torch
+
+    return torch.empty((max(backward_workspace_size(cfg), 256),), dtype=torch.uint8, device=device)
+
+
+def _zero_grads(cfg: EngramConfig, dev):
+    import torch
+
+    E, d, hc = cfg.emb_dim, cfg.hidden, cfg.hc_mult
+    rows = sum(int(cfg.primes[h]) for h in range(cfg.n_heads))
+    shapes = {"d_tables": (rows, cfg.head_dim), "d_w_kv": ((hc + 1) * d, E), "d_gamma_k": (hc, d),
+              "d_gamma_q": (hc, d), "d_conv_w": (hc, d, cfg.conv_kernel)}
+    return {k: torch.zeros(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+
+
 def backward(cfg: EngramConfig, p: Params, ids, hidden, dy, grads=None, d_hidden=None, workspace=None, stream=None):
     """Gradients of Engram.forward for an upstream gradient dy.  `grads`: dict
     of float32 tensors named GRAD_NAMES, added to (allocated as zeros when
@@ -429,20 +453,43 @@ def backward(cfg: EngramConfig, p: Params, ids, hidden, dy, grads=None, d_hidden
 
     dev = ids.device
     if grads is None:
-        E, d, hc = cfg.emb_dim, cfg.hidden, cfg.hc_mult
-        rows = sum(int(cfg.primes[h]) for h in range(cfg.n_heads))
-        shapes = {"d_tables": (rows, cfg.head_dim), "d_w_kv": ((hc + 1) * d, E), "d_gamma_k": (hc, d),
-                  "d_gamma_q": (hc, d), "d_conv_w": (hc, d, cfg.conv_kernel)}
-        grads = {k: torch.zeros(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+        grads = _zero_grads(cfg, dev)
     if d_hidden is None:
         d_hidden = torch.empty_like(hidden)
     if workspace is None:
-        n = load().engram_backward_workspace_size(ctypes.byref(cfg))
-        workspace = torch.empty((max(n, 256),), dtype=torch.uint8, device=dev)
+        workspace = alloc_backward_workspace(cfg, dev)
     rc = load().engram_backward(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), _ptr(dy),
                                 _ptr(d_hidden), *[_ptr(grads[k]) for k in GRAD_NAMES], _ptr(workspace),
                                 workspace.numel(), _stream(stream))
     _check("engram_backward", rc)
+    return d_hidden, grads
+
+
+def forward_train(cfg: EngramConfig, p: Params, ids, hidden, workspace, out=None, stream=None):
+    """Forward of a training step; `workspace` (alloc_backward_workspace) keeps
+    what backward_saved needs.  Returns out [B][T][hc][d]."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(hidden)
+    rc = load().engram_forward_train(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("engram_forward_train", rc)
+    return out
+
+
+def backward_saved(cfg: EngramConfig, p: Params, hidden, dy, workspace, grads=None, d_hidden=None, stream=None):
+    """backward on the quantities forward_train kept in `workspace`.  Returns (d_hidden, grads)."""
+    import torch
+
+    if grads is None:
+        grads = _zero_grads(cfg, hidden.device)
+    if d_hidden is None:
+        d_hidden = torch.empty_like(hidden)
+    rc = load().engram_backward_saved(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(hidden), _ptr(dy), _ptr(d_hidden),
+                                      *[_ptr(grads[k]) for k in GRAD_NAMES], _ptr(workspace), workspace.numel(),
+                                      _stream(stream))
+    _check("engram_backward_saved", rc)
     return d_hidden, grads
 
 

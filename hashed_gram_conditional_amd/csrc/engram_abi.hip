@@ -163,13 +163,19 @@ struct BwdWorkspace {
   int32_t* idx;     // [N][H]
   void* kv;         // [N][hc+1][d]
   float4* stats;    // [N][hc] (g, s, rk, rq)
-  float* dvg;       // [N][hc][d]
+  float* g;         // [N][hc] gates (the conv of engram_forward_train reads them)
+  void* dvg;        // [N][hc][d] dtype: gradient of the gated values
   void* dkv;        // [N][hc+1][d]
   float* de;        // [N][E]
   void* wT;         // [E][(hc+1)d]
-  void* dkvT;       // [(hc+1)d][Np]
-  void* eT;         // [E][Np]
-  int64_t Np;
+  void* dkvT;       // [S][(hc+1)d][Np/S]: token axis in S split-K chunks
+  void* eT;         // [S][E][Np/S]
+  float* wpart;     // [S][(hc+1)d][E] when S > 1: the splits' products
+  float* gpart;     // [gate_bwd_rows(N)][hc][d]: per-block sums for the gammas' gradients
+  float* cpart;     // [conv_bwd_rows][hc][d][K]: per-block sums for the taps' gradients
+  int64_t Np;       // S chunks of Ks tokens (multiples of 64), zero past N
+  int64_t Ks;
+  int S;
   size_t bytes;
 };
 
@@ -177,7 +183,9 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   const int64_t N = (int64_t)c->batch * c->seqlen, E = emb_dim(c), O = (int64_t)(c->hc_mult + 1) * c->hidden;
   const int64_t es = esize(c);
   BwdWorkspace w = {};
-  w.Np = (N + 63) / 64 * 64;
+  w.S = c->dtype == ENGRAM_BF16 ? gemm_k_splits(O, E, N) : 1;
+  w.Ks = (N + (int64_t)w.S * 64 - 1) / ((int64_t)w.S * 64) * 64;
+  w.Np = w.S * w.Ks;
   size_t off = 0;
   auto take = [&](size_t n) {
     void* p = (uint8_t*)base + off;
@@ -188,12 +196,17 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.idx = (int32_t*)take((size_t)N * n_heads(c) * sizeof(int32_t));
   w.kv = take((size_t)(N * O * es));
   w.stats = (float4*)take((size_t)N * c->hc_mult * sizeof(float4));
-  w.dvg = (float*)take((size_t)N * c->hc_mult * c->hidden * sizeof(float));
+  w.g = (float*)take((size_t)N * c->hc_mult * sizeof(float));
+  w.dvg = take((size_t)(N * c->hc_mult * c->hidden * es));
   w.dkv = take((size_t)(N * O * es));
   w.de = (float*)take((size_t)(N * E) * sizeof(float));
   w.wT = take((size_t)(E * O * es));
   w.dkvT = take((size_t)(O * w.Np * es));
   w.eT = take((size_t)(E * w.Np * es));
+  w.wpart = w.S > 1 ? (float*)take((size_t)w.S * O * E * sizeof(float)) : nullptr;
+  w.gpart = (float*)take((size_t)gate_bwd_rows(N) * c->hc_mult * c->hidden * sizeof(float));
+  w.cpart = (float*)take((size_t)conv_bwd_rows(c->batch, c->seqlen) * c->hc_mult * c->hidden * c->conv_kernel *
+                         sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -382,6 +395,139 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   return ENGRAM_OK;
 }
 
+// Checks shared by the backward entry points (ids only when the forward
+// quantities are recomputed).
+engram_status check_backward(const engram_config* cfg, const engram_params* prm, bool need_ids, const int32_t* ids,
+                             const void* hidden, const void* dy, void* d_hidden, float* d_tables, float* d_w_kv,
+                             float* d_gamma_k, float* d_gamma_q, float* d_conv_w, void* workspace,
+                             size_t workspace_bytes) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if ((rc = need_ids ? check_params(cfg, prm) : check_params_no_tables(cfg, prm))) return rc;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if ((need_ids && ids == nullptr) || hidden == nullptr || dy == nullptr || d_hidden == nullptr ||
+      d_tables == nullptr || d_w_kv == nullptr || d_gamma_k == nullptr || d_gamma_q == nullptr ||
+      d_conv_w == nullptr || workspace == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(dy, 16) || !aligned(d_hidden, 16) || !aligned(workspace, 256) ||
+      !aligned(d_tables, 4) || !aligned(d_w_kv, 4) || !aligned(d_gamma_k, 4) || !aligned(d_gamma_q, 4) ||
+      !aligned(d_conv_w, 4))
+    return ENGRAM_EINVAL;
+  if (workspace_bytes < carve_bwd(cfg, nullptr).bytes) return ENGRAM_ENOMEM;
+  return ENGRAM_OK;
+}
+
+// The forward quantities the gradients need, into the workspace: rows and
+// indices, K/V, the gate statistics (and the gates alone, for a conv).
+hipError_t forward_quantities(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                              const void* hidden, const BwdWorkspace& w, hipStream_t stream) {
+  const bool bf16 = cfg->dtype == ENGRAM_BF16;
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  hipError_t e;
+  GatherArgs ga = gather_args(cfg, prm, ids, nullptr);
+  ga.idx_out = w.idx;
+  ga.e_out = (uint8_t*)w.e;
+  if ((e = launch_hash_gather(hc, ga, true, stream, gather_grid_cap(prm->tables)))) return e;
+  const GemmArgs gm = gemm_args(cfg, prm, w.e, w.kv);
+  if ((e = bf16 ? launch_gemm_bf16(gm, stream) : launch_gemm_f32(gm, stream))) return e;
+  GateArgs gt = gate_args(cfg, prm, w.kv, hidden, w.g);
+  gt.stats = w.stats;
+  return launch_gate(gt, stream);
+}
+
+// Gradients from the forward quantities in the workspace.
+engram_status gradients(const engram_config* cfg, const engram_params* prm, const void* hidden, const void* dy,
+                        void* d_hidden, float* d_tables, float* d_w_kv, float* d_gamma_k, float* d_gamma_q,
+                        float* d_conv_w, const BwdWorkspace& w, hipStream_t stream) {
+  const int64_t N = (int64_t)cfg->batch * cfg->seqlen;
+  const bool bf16 = cfg->dtype == ENGRAM_BF16;
+  const int64_t E = emb_dim(cfg), O = (int64_t)(cfg->hc_mult + 1) * cfg->hidden;
+  const int es = (int)esize(cfg);
+  HashConsts hc;
+  make_hash_consts(cfg, &hc);
+  hipError_t e;
+  // conv, gate, value fusion
+  ConvBwdArgs cb;
+  cb.dy = dy;
+  cb.kv = w.kv;
+  cb.stats = w.stats;
+  cb.conv_w = prm->conv_w;
+  cb.dvg = w.dvg;
+  cb.part = w.cpart;
+  cb.span = conv_bwd_span(N);
+  cb.batch = cfg->batch;
+  cb.seqlen = cfg->seqlen;
+  cb.hc = cfg->hc_mult;
+  cb.d = cfg->hidden;
+  cb.ksize = cfg->conv_kernel;
+  cb.dil = cfg->conv_dilation;
+  cb.bf16 = bf16;
+  if ((e = launch_conv_bwd(cb, stream))) return hip_status(e);
+  GateBwdArgs gb;
+  gb.dvg = w.dvg;
+  gb.kv = w.kv;
+  gb.hidden = hidden;
+  gb.gamma_k = prm->gamma_k;
+  gb.gamma_q = prm->gamma_q;
+  gb.stats = w.stats;
+  gb.dkv = w.dkv;
+  gb.d_hidden = d_hidden;
+  gb.part = w.gpart;
+  gb.n_tok = (int32_t)N;
+  gb.tpb = gate_bwd_tpb(N);
+  gb.hc = cfg->hc_mult;
+  gb.d = cfg->hidden;
+  gb.clamp = cfg->gate_clamp;
+  gb.inv_sqrt_d = (float)(1.0 / sqrt((double)cfg->hidden));
+  gb.bf16 = bf16;
+  if ((e = launch_gate_bwd(gb, stream))) return hip_status(e);
+  // sums over tokens: d gamma_k = gamma_q S, d gamma_q = gamma_k S; the taps
+  if ((e = launch_colsum(w.gpart, gate_bwd_rows(N), (int64_t)cfg->hc_mult * cfg->hidden, d_gamma_k, prm->gamma_q,
+                         d_gamma_q, prm->gamma_k, bf16, stream)))
+    return hip_status(e);
+  if ((e = launch_colsum(w.cpart, conv_bwd_rows(cfg->batch, cfg->seqlen),
+                         (int64_t)cfg->hc_mult * cfg->hidden * cfg->conv_kernel, d_conv_w, nullptr, nullptr, nullptr,
+                         bf16, stream)))
+    return hip_status(e);
+  // de = dKV W (into float32), then the rows' gradients
+  if ((e = launch_transpose(prm->w_kv, w.wT, O, E, O, es, stream))) return hip_status(e);
+  GemmArgs g1;
+  g1.A = w.dkv;
+  g1.B = w.wT;
+  g1.C = w.de;
+  g1.M = (int32_t)N;
+  g1.N = (int32_t)E;
+  g1.K = (int32_t)O;
+  g1.accumulate = 0;
+  if ((e = bf16 ? launch_gemm_bf16_f32out(g1, stream) : launch_gemm_f32(g1, stream))) return hip_status(e);
+  if ((e = launch_scatter_add(hc, w.idx, w.de, d_tables, N, cfg->head_dim, stream))) return hip_status(e);
+  // dW += dKV^T e
+  // (in S split-K chunks of the token axis when the output has too few tiles
+  // to fill the chip; the chunks' products are then added in chunk order)
+  const int64_t chunk = w.S > 1 ? w.Ks : 0;
+  if ((e = launch_transpose(w.dkv, w.dkvT, N, O, w.Np, es, stream, chunk))) return hip_status(e);
+  if ((e = launch_transpose(w.e, w.eT, N, E, w.Np, es, stream, chunk))) return hip_status(e);
+  GemmArgs g2;
+  g2.A = w.dkvT;
+  g2.B = w.eT;
+  g2.C = w.S > 1 ? (void*)w.wpart : (void*)d_w_kv;
+  g2.M = (int32_t)O;
+  g2.N = (int32_t)E;
+  g2.K = (int32_t)w.Ks;
+  g2.accumulate = w.S > 1 ? 0 : 1;
+  g2.splits = w.S;
+  g2.split_a = O * w.Ks;
+  g2.split_b = E * w.Ks;
+  g2.split_c = O * E;
+  if ((e = bf16 ? launch_gemm_bf16_f32out(g2, stream) : launch_gemm_f32(g2, stream))) return hip_status(e);
+  if (w.S > 1 &&
+      (e = launch_colsum(w.wpart, w.S, O * E, d_w_kv, nullptr, nullptr, nullptr, bf16, stream)))
+    return hip_status(e);
+  return ENGRAM_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -522,95 +668,43 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* prm
                               const void* hidden, const void* dy, void* d_hidden, float* d_tables, float* d_w_kv,
                               float* d_gamma_k, float* d_gamma_q, float* d_conv_w, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
+  engram_status rc = check_backward(cfg, prm, true, ids, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k,
+                                    d_gamma_q, d_conv_w, workspace, workspace_bytes);
+  if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
+  const BwdWorkspace w = carve_bwd(cfg, workspace);
+  hipError_t e;
+  if ((e = forward_quantities(cfg, prm, ids, hidden, w, stream))) return hip_status(e);
+  return gradients(cfg, prm, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k, d_gamma_q, d_conv_w, w, stream);
+}
+
+engram_status engram_forward_train(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                   const void* hidden, void* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
   engram_status rc = validate(cfg);
   if (rc) return rc;
   if ((rc = check_params(cfg, prm))) return rc;
-  const int64_t N = (int64_t)cfg->batch * cfg->seqlen;
-  if (N == 0) return ENGRAM_OK;
-  if (ids == nullptr || hidden == nullptr || dy == nullptr || d_hidden == nullptr || d_tables == nullptr ||
-      d_w_kv == nullptr || d_gamma_k == nullptr || d_gamma_q == nullptr || d_conv_w == nullptr || workspace == nullptr)
-    return ENGRAM_EINVAL;
-  if (!aligned(hidden, 16) || !aligned(dy, 16) || !aligned(d_hidden, 16) || !aligned(workspace, 256) ||
-      !aligned(d_tables, 4) || !aligned(d_w_kv, 4) || !aligned(d_gamma_k, 4) || !aligned(d_gamma_q, 4) ||
-      !aligned(d_conv_w, 4))
-    return ENGRAM_EINVAL;
+  if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (ids == nullptr || hidden == nullptr || out == nullptr || workspace == nullptr) return ENGRAM_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(workspace, 256)) return ENGRAM_EINVAL;
   const BwdWorkspace w = carve_bwd(cfg, workspace);
   if (workspace_bytes < w.bytes) return ENGRAM_ENOMEM;
-  const bool bf16 = cfg->dtype == ENGRAM_BF16;
-  const int64_t E = emb_dim(cfg), O = (int64_t)(cfg->hc_mult + 1) * cfg->hidden;
-  const int es = (int)esize(cfg);
-  HashConsts hc;
-  make_hash_consts(cfg, &hc);
   hipError_t e;
-  // forward quantities: rows, indices, projections, gate statistics
-  GatherArgs ga = gather_args(cfg, prm, ids, nullptr);
-  ga.idx_out = w.idx;
-  ga.e_out = (uint8_t*)w.e;
-  if ((e = launch_hash_gather(hc, ga, true, stream, gather_grid_cap(prm->tables)))) return hip_status(e);
-  const GemmArgs gm = gemm_args(cfg, prm, w.e, w.kv);
-  if ((e = bf16 ? launch_gemm_bf16(gm, stream) : launch_gemm_f32(gm, stream))) return hip_status(e);
-  GateArgs gt = gate_args(cfg, prm, w.kv, hidden, nullptr);
-  gt.stats = w.stats;
-  if ((e = launch_gate(gt, stream))) return hip_status(e);
-  // conv, gate, value fusion
-  ConvBwdArgs cb;
-  cb.dy = dy;
-  cb.kv = w.kv;
-  cb.stats = w.stats;
-  cb.conv_w = prm->conv_w;
-  cb.dvg = w.dvg;
-  cb.d_conv_w = d_conv_w;
-  cb.batch = cfg->batch;
-  cb.seqlen = cfg->seqlen;
-  cb.hc = cfg->hc_mult;
-  cb.d = cfg->hidden;
-  cb.ksize = cfg->conv_kernel;
-  cb.dil = cfg->conv_dilation;
-  cb.bf16 = bf16;
-  if ((e = launch_conv_bwd(cb, stream))) return hip_status(e);
-  GateBwdArgs gb;
-  gb.dvg = w.dvg;
-  gb.kv = w.kv;
-  gb.hidden = hidden;
-  gb.gamma_k = prm->gamma_k;
-  gb.gamma_q = prm->gamma_q;
-  gb.stats = w.stats;
-  gb.dkv = w.dkv;
-  gb.d_hidden = d_hidden;
-  gb.d_gamma_k = d_gamma_k;
-  gb.d_gamma_q = d_gamma_q;
-  gb.n_tok = (int32_t)N;
-  gb.hc = cfg->hc_mult;
-  gb.d = cfg->hidden;
-  gb.clamp = cfg->gate_clamp;
-  gb.inv_sqrt_d = (float)(1.0 / sqrt((double)cfg->hidden));
-  gb.bf16 = bf16;
-  if ((e = launch_gate_bwd(gb, stream))) return hip_status(e);
-  // de = dKV W (into float32), then the rows' gradients
-  if ((e = launch_transpose(prm->w_kv, w.wT, O, E, O, es, stream))) return hip_status(e);
-  GemmArgs g1;
-  g1.A = w.dkv;
-  g1.B = w.wT;
-  g1.C = w.de;
-  g1.M = (int32_t)N;
-  g1.N = (int32_t)E;
-  g1.K = (int32_t)O;
-  g1.accumulate = 0;
-  if ((e = bf16 ? launch_gemm_bf16_f32out(g1, stream) : launch_gemm_f32(g1, stream))) return hip_status(e);
-  if ((e = launch_scatter_add(hc, w.idx, w.de, d_tables, N, cfg->head_dim, stream))) return hip_status(e);
-  // dW += dKV^T e
-  if ((e = launch_transpose(w.dkv, w.dkvT, N, O, w.Np, es, stream))) return hip_status(e);
-  if ((e = launch_transpose(w.e, w.eT, N, E, w.Np, es, stream))) return hip_status(e);
-  GemmArgs g2;
-  g2.A = w.dkvT;
-  g2.B = w.eT;
-  g2.C = d_w_kv;
-  g2.M = (int32_t)O;
-  g2.N = (int32_t)E;
-  g2.K = (int32_t)w.Np;
-  g2.accumulate = 1;
-  if ((e = bf16 ? launch_gemm_bf16_f32out(g2, stream) : launch_gemm_f32(g2, stream))) return hip_status(e);
+  if ((e = forward_quantities(cfg, prm, ids, hidden, w, stream))) return hip_status(e);
+  const void* v = (const uint8_t*)w.kv + (int64_t)cfg->hc_mult * cfg->hidden * esize(cfg);
+  const ConvArgs cv = conv_args(cfg, prm, v, (int64_t)(cfg->hc_mult + 1) * cfg->hidden, w.g, out, nullptr);
+  if ((e = launch_conv(cv, stream))) return hip_status(e);
   return ENGRAM_OK;
+}
+
+engram_status engram_backward_saved(const engram_config* cfg, const engram_params* prm, const void* hidden,
+                                    const void* dy, void* d_hidden, float* d_tables, float* d_w_kv,
+                                    float* d_gamma_k, float* d_gamma_q, float* d_conv_w, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  engram_status rc = check_backward(cfg, prm, false, nullptr, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k,
+                                    d_gamma_q, d_conv_w, workspace, workspace_bytes);
+  if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
+  return gradients(cfg, prm, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k, d_gamma_q, d_conv_w,
+                   carve_bwd(cfg, workspace), stream);
 }
 
 engram_status engram_gather_host(const engram_config* cfg, const void* tables, const int32_t* idx, void* e_out,

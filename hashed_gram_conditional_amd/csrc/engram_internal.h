@@ -79,7 +79,13 @@ struct GemmArgs {
   void* C;         // kv  [M][N]
   int32_t M, N, K;
   int32_t accumulate = 0;   // float32 outputs: C += A B^T instead of C = A B^T
+  // float32 outputs only: `splits` independent products in one launch, the
+  // s-th on A + s split_a, B + s split_b into C + s split_c (elements)
+  int32_t splits = 1;
+  int64_t split_a = 0, split_b = 0, split_c = 0;
 };
+// split-K count for a float32-output product of M x N over a long K (1 = none)
+int gemm_k_splits(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 // bf16 operands, float32 result stored or accumulated into C (a.accumulate)
@@ -150,16 +156,21 @@ struct ConvBwdArgs {
   const void* kv;          // [N][hc+1][d] (values in the last block)
   const float4* stats;     // [N][hc] (g, s, rk, rq)
   const void* conv_w;      // [hc][d][K]
-  float* dvg;              // [N][hc][d]
-  float* d_conv_w;         // [hc][d][K], added to
+  void* dvg;               // [N][hc][d] dtype
+  float* part;             // [conv_bwd_rows][hc][d][K]: tap sums of each block's positions
   int32_t batch, seqlen, hc, d, ksize, dil;
+  int32_t span;            // positions per thread (a block covers 4 spans of one sequence)
   bool bf16;
 };
+// positions per thread of the conv backward, and the partial rows it writes
+int conv_bwd_span(int64_t n_tok);
+int64_t conv_bwd_rows(int32_t batch, int32_t seqlen);
 hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
 
-// gate and RMSNorm gradients (dK, d hidden, d gammas), and dV
+// gate and RMSNorm gradients (dK, d hidden) and dV; the gammas' gradients as
+// per-block partial sums S = sum_n coef K Q (d gamma_k = gamma_q S, d gamma_q = gamma_k S)
 struct GateBwdArgs {
-  const float* dvg;        // [N][hc][d]
+  const void* dvg;         // [N][hc][d] dtype
   const void* kv;          // [N][hc+1][d]
   const void* hidden;      // [N][hc][d]
   const void* gamma_k;     // [hc][d]
@@ -167,17 +178,25 @@ struct GateBwdArgs {
   const float4* stats;     // [N][hc]
   void* dkv;               // [N][hc+1][d]: dK blocks and dV
   void* d_hidden;          // [N][hc][d]
-  float* d_gamma_k;        // [hc][d], added to
-  float* d_gamma_q;
+  float* part;             // [gate_bwd_rows][hc][d]
   int32_t n_tok, hc, d;
+  int32_t tpb;             // tokens per block
   float clamp, inv_sqrt_d;
   bool bf16;
 };
+int gate_bwd_tpb(int64_t n_tok);
+int64_t gate_bwd_rows(int64_t n_tok);
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 
-// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < ld_dst (elements of esz bytes)
+// out0[c] += scale0[c] * sum_r part[r][c] (scale0 NULL: 1), and the same sum
+// into out1 with scale1 when out1 is not NULL; rows summed in a fixed order
+hipError_t launch_colsum(const float* part, int64_t rows, int64_t cols, float* out0, const void* scale0,
+                         float* out1, const void* scale1, bool bf16, hipStream_t s);
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < ld_dst (elements of
+// esz bytes; cols and ld_dst multiples of 16 / esz).  chunk > 0 (a multiple of
+// 64 dividing ld_dst): the r axis in chunks, dst[r / chunk][c][r % chunk].
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, int64_t ld_dst, int esz,
-                            hipStream_t s);
+                            hipStream_t s, int64_t chunk = 0);
 
 // d_tables[row_off[h] + idx[n][h]][j] += de[n][h*Dh + j]
 hipError_t launch_scatter_add(const HashConsts& hc, const int32_t* idx, const float* de, float* d_tables,

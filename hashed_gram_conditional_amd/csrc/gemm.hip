@@ -165,14 +165,19 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: DMA LDS addresses stay scalar
   const int wm = wave % WM, wn = wave / WM;
   const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
+  // split-K batches are stacked along M in the tile order
   int mt, nt;
-  tile_of(blockIdx.x, m_tiles, n_tiles, mt, nt);
+  tile_of(blockIdx.x, a.splits * m_tiles, n_tiles, mt, nt);
+  const int split = mt / m_tiles;
+  mt -= split * m_tiles;
   const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
   const int K = a.K;
   const int nk = (K + BK - 1) / BK;
   const int nk_pad = (nk + kStages - 1) / kStages * kStages;
-  const __amdgpu_buffer_rsrc_t rA = tile_rsrc((const uint16_t*)a.A, m0, min((int64_t)BM, a.M - m0), K);
-  const __amdgpu_buffer_rsrc_t rB = tile_rsrc((const uint16_t*)a.B, n0, min((int64_t)BN, a.N - n0), K);
+  const __amdgpu_buffer_rsrc_t rA =
+      tile_rsrc((const uint16_t*)a.A + split * a.split_a, m0, min((int64_t)BM, a.M - m0), K);
+  const __amdgpu_buffer_rsrc_t rB =
+      tile_rsrc((const uint16_t*)a.B + split * a.split_b, n0, min((int64_t)BN, a.N - n0), K);
   const int row_bytes = K * 2;
 
   // this lane's slot in the block of rows one DMA instruction fills: tile row
@@ -410,7 +415,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 
   if constexpr (F32OUT) {
     // float32 result (gradients): 4 consecutive columns per lane, stored or added
-    float* __restrict__ C = (float*)a.C;
+    float* __restrict__ C = (float*)a.C + split * a.split_c;
 #pragma unroll
     for (int j = 0; j < TM; j++) {
       const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
@@ -600,7 +605,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
 
 template <int BM, int BN, int WM, int WN, int ST, bool GATE, bool F32OUT = false>
 hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
-  const int64_t tiles = (int64_t)((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
+  const int64_t tiles = (int64_t)a.g.splits * ((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
   k_gemm_bf16<BM, BN, WM, WN, ST, GATE, F32OUT><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -626,10 +631,33 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   return gemm_launch<128, 128, 2, 2, 2, false>(ga, s);
 }
 
+int gemm_k_splits(int64_t M, int64_t N, int64_t K) {
+  // A long K over few output tiles: with S splits the time goes as the rounds
+  // of 256-wide tiles over 256 CUs, ceil(S tiles / 256), times K / S.  Take
+  // the S <= 8 that minimises it (each split at least 4096 deep, and whole
+  // 256 x 256 tiles at least twice the CUs), if it beats one split by 10%.
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int best = 1;
+  double best_cost = (double)((tiles + 255) / 256);
+  for (int S = 2; S <= 8; S++) {
+    if (K / S < 4096 || S * tiles < 2 * 256) continue;
+    const double cost = (double)((S * tiles + 255) / 256) / S;
+    if (cost < 0.9 * best_cost) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   GemmGateArgs ga = {};
   ga.g = a;
+  // 256 x 256 tiles once they fill the chip twice over (fewer L2 requests per flop)
+  if ((int64_t)a.splits * ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 2 * 256)
+    return gemm_launch<256, 256, 4, 2, 2, false, true>(ga, s);
+  if (a.splits != 1) return hipErrorInvalidValue;
   if (few_tiles(a.M, a.N)) return gemm_launch<128, 128, 2, 2, 4, false, true>(ga, s);
   return gemm_launch<128, 128, 2, 2, 2, false, true>(ga, s);
 }

@@ -204,8 +204,9 @@ size_t engram_backward_workspace_size(const engram_config *cfg);
  *   d_gamma_k, d_gamma_q [hc_mult][hidden], d_conv_w [hc_mult][hidden][conv_kernel]:
  *   float32, ADDED to (zero them for plain gradients; only the table rows the
  *   hashes select change).
- * Sums across tokens (table rows, gammas, taps) use float32 atomics, so their
- * last bits may differ between runs; the gradients must be device memory.
+ * The table rows' sums over tokens use float32 atomics, so their last bits may
+ * differ between runs (the gammas' and taps' sums are taken in a fixed order);
+ * the gradients must be device memory.
  * workspace: device memory of at least engram_backward_workspace_size(cfg)
  * bytes, 256-byte aligned.  ENGRAM_EINVAL for a NULL or misaligned pointer
  * (hidden, dy, d_hidden 16-byte aligned), ENGRAM_ENOMEM for a short workspace,
@@ -215,6 +216,28 @@ engram_status engram_backward(const engram_config *cfg, const engram_params *prm
                               const void *hidden, const void *dy, void *d_hidden, float *d_tables, float *d_w_kv,
                               float *d_gamma_k, float *d_gamma_q, float *d_conv_w, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* The forward of a training step (no state): the same output as
+ * engram_forward, within rounding (the gate's sums are taken by a separate
+ * kernel rather than in the projection's epilogue), that also keeps in
+ * `workspace` the forward quantities the gradients need: the gathered rows,
+ * their indices, K/V and the gate statistics.  workspace: device memory of at
+ * least engram_backward_workspace_size(cfg) bytes, 256-byte aligned, owned by
+ * the caller and left untouched until the matching engram_backward_saved.
+ * ENGRAM_EINVAL / ENGRAM_ENOMEM as engram_forward, before anything is launched. */
+engram_status engram_forward_train(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                   const void *hidden, void *out, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* engram_backward on the forward quantities that engram_forward_train left in
+ * `workspace` (same cfg, parameters and hidden; issued after it on the same
+ * stream or ordered by an event): the recomputation is skipped, so neither the
+ * ids nor the tables are read (prm->tables may be NULL).  Gradients, their
+ * accumulation and the errors as engram_backward. */
+engram_status engram_backward_saved(const engram_config *cfg, const engram_params *prm, const void *hidden,
+                                    const void *dy, void *d_hidden, float *d_tables, float *d_w_kv,
+                                    float *d_gamma_k, float *d_gamma_q, float *d_conv_w, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* Same as engram_forward, additionally recording events[2i] / events[2i+1]
  * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,

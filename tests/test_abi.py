@@ -207,3 +207,32 @@ def test_backward_validates_on_the_host(eg):
     assert f(ctypes.byref(c), ctypes.byref(prm), *ok, None, ws, None) == -1
     empty = good(eg, batch=0)
     assert f(ctypes.byref(empty), ctypes.byref(prm), *([None] * 9), None, 0, None) == 0
+
+
+def test_forward_train_and_backward_saved_validate_on_the_host(eg):
+    """engram_forward_train needs ids, hidden, out and a backward-sized
+    workspace; engram_backward_saved needs no ids and no tables."""
+    c = good(eg)
+    lib = eg.load()
+    P = ctypes.c_void_p
+    prm = eg._Params(P(16), P(16), P(16), P(16), P(16), P(16))
+    no_tables = eg._Params(P(16), None, P(16), P(16), P(16), P(16))
+    ws = lib.engram_backward_workspace_size(ctypes.byref(c))
+    f = lib.engram_forward_train
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), P(16), P(16), P(256), ws - 1, None) == -2
+    assert f(ctypes.byref(c), ctypes.byref(no_tables), P(16), P(16), P(16), P(256), ws, None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), None, P(16), P(16), P(256), ws, None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), P(24), P(16), P(256), ws, None) == -1
+    assert f(ctypes.byref(c), ctypes.byref(prm), P(16), P(16), P(16), P(128), ws, None) == -1
+    g = lib.engram_backward_saved
+    ok = [P(16)] * 8
+    assert g(ctypes.byref(c), ctypes.byref(no_tables), *ok, P(256), ws - 1, None) == -2
+    for i in range(len(ok)):
+        args = list(ok)
+        args[i] = None
+        assert g(ctypes.byref(c), ctypes.byref(no_tables), *args, P(256), ws, None) == -1, i
+    no_w = eg._Params(P(16), None, None, P(16), P(16), P(16))
+    assert g(ctypes.byref(c), ctypes.byref(no_w), *ok, P(256), ws, None) == -1
+    empty = good(eg, batch=0)
+    assert f(ctypes.byref(empty), ctypes.byref(prm), None, None, None, None, 0, None) == 0
+    assert g(ctypes.byref(empty), ctypes.byref(no_tables), *([None] * 8), None, 0, None) == 0

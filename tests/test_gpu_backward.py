@@ -110,3 +110,54 @@ def test_backward_accumulates(eg):
     for k in grads2:
         assert normwise(grads2[k].double().cpu().numpy(), 2 * got[k]) <= 1e-6, k
     assert torch.equal(dh2, dh)
+
+
+@pytest.mark.parametrize("name,over", [("tiny_fp32", {}), ("b4_t1024", dict(batch=2, seqlen=200, prime_base=4001))])
+def test_forward_train_matches_oracle(eg, name, over):
+    """engram_forward_train's output, at every position, within the dtype's bar."""
+    c = Case(name, **over)
+    ws = eg.alloc_backward_workspace(c.cfg())
+    y = eg.forward_train(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"], ws)
+    torch.cuda.synchronize()
+    N = c.B * c.T
+    pos = np.arange(N)
+    got = y.to(torch.float64).cpu().numpy().reshape(N, c.w.hc_mult, c.w.hidden)
+    assert normwise(got, c.y_at_many(pos)) <= TOL[c.w.dtype]
+
+
+@pytest.mark.parametrize("name,over", [("tiny_fp32", {}), ("b4_t1024", dict(batch=2, seqlen=200, prime_base=4001))])
+def test_backward_saved_equals_recompute(eg, name, over):
+    """engram_backward_saved after engram_forward_train gives engram_backward's
+    gradients: the same kernels on the same forward quantities, so every
+    gradient is bit-equal except the table rows' (atomic order), and the
+    tables are not read (NULL in the parameters)."""
+    c = Case(name, **over)
+    cfg = c.cfg()
+    ws = eg.alloc_backward_workspace(cfg)
+    hid = c.dev["hidden"]
+    dy = torch.randn(hid.shape, generator=torch.Generator().manual_seed(5), dtype=torch.float32).to(hid.dtype)
+    dy = dy.to("cuda")
+    eg.forward_train(cfg, c.params, c.dev["ids"], hid, ws)
+    d = c.dev
+    no_tables = eg.Params(remap=d["remap"], tables=None, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                          conv_w=d["conv_w"])
+    dh_s, g_s = eg.backward_saved(cfg, no_tables, hid, dy, ws)
+    dh_r, g_r = eg.backward(cfg, c.params, d["ids"], hid, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(dh_s, dh_r)
+    for k in ("d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w"):
+        assert torch.equal(g_s[k], g_r[k]), k
+    assert normwise(g_s["d_tables"].double().cpu().numpy(), g_r["d_tables"].double().cpu().numpy()) <= 1e-6
+
+
+def test_gamma_and_tap_gradients_are_deterministic(eg):
+    """The gammas' and taps' sums over tokens are taken in a fixed order: two calls give the same bits."""
+    c = Case("b4_t1024", batch=2, seqlen=200, prime_base=4001)
+    hid = c.dev["hidden"]
+    dy = torch.randn(hid.shape, generator=torch.Generator().manual_seed(6), dtype=torch.float32).to(hid.dtype)
+    dy = dy.to("cuda")
+    _, g1 = eg.backward(c.cfg(), c.params, c.dev["ids"], hid, dy)
+    _, g2 = eg.backward(c.cfg(), c.params, c.dev["ids"], hid, dy)
+    torch.cuda.synchronize()
+    for k in ("d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w"):
+        assert torch.equal(g1[k], g2[k]), k

@@ -51,6 +51,7 @@ STREAM_GAMMA_K = 8       # RMSNorm scale on keys
 STREAM_GAMMA_Q = 9       # RMSNorm scale on queries
 STREAM_CONV = 10         # short-conv taps
 STREAM_HIDDEN = 11       # hidden states (queries)
+STREAM_DY = 12           # upstream gradient of the module's output (backward tests)
 
 
 def mix64(z: np.ndarray) -> np.ndarray:
@@ -337,6 +338,17 @@ class Inputs:
         return real_array(w.seed, STREAM_HIDDEN, c, w.sigma_hidden, 0.0, w.dtype).reshape(
             len(b), w.hc_mult, w.hidden)
 
+    def dy_at(self, b, t) -> np.ndarray:
+        """An upstream gradient dL/dy at (b, t) for index arrays b, t -> [len][hc][d]
+        in storage form (same shape and spread as the hidden states)."""
+        w = self.w
+        b = np.asarray(b, dtype=np.int64)
+        t = np.asarray(t, dtype=np.int64)
+        per = w.hc_mult * w.hidden
+        base = (b * self.seq_total + t) * per
+        c = base[:, None] + np.arange(per, dtype=np.int64)[None, :]
+        return real_array(w.seed, STREAM_DY, c, w.sigma_hidden, 0.0, w.dtype).reshape(len(b), w.hc_mult, w.hidden)
+
     def hidden(self) -> np.ndarray:
         n = int(np.prod(self.hidden_shape()))
         return real_array(self.w.seed, STREAM_HIDDEN, np.arange(n), self.w.sigma_hidden, 0.0,
@@ -352,4 +364,5 @@ class Inputs:
             "gamma_q": (STREAM_GAMMA_Q, w.sigma_gamma, 1.0),
             "conv_w": (STREAM_CONV, w.sigma_conv, 0.0),
             "hidden": (STREAM_HIDDEN, w.sigma_hidden, 0.0),
+            "dy": (STREAM_DY, w.sigma_hidden, 0.0),
         }[name]

@@ -77,8 +77,9 @@ def _load():
         lib.orc_forward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P]
         lib.orc_forward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, ctypes.c_int64, P, P]
         lib.orc_backward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_backward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, rp, ctypes.c_int64, P, P, P]
         for f in ("orc_shift", "orc_hash", "orc_gather", "orc_project", "orc_gate", "orc_conv", "orc_forward",
-                  "orc_forward_at", "orc_backward"):
+                  "orc_forward_at", "orc_backward", "orc_backward_at"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -274,6 +275,29 @@ class Oracle:
                                  *[_p(out[k]) for k in ("d_table", "d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w",
                                                        "d_hidden")]), "orc_backward")
         return out
+
+    def backward_at(self, ids, remap, table, w_kv, gamma_k, gamma_q, conv_w, hidden, dy, positions,
+                    table_keys=None, hidden_keys=None, dy_keys=None, want_de: bool = True):
+        """orc_backward_at: (d_hidden [P][hc][d], de [P][E] or None) at flat positions.
+        table, hidden and dy may be sparse (rows + ascending keys); hidden and dy
+        rows are keyed by flat position, [hc][d] each, in storage form."""
+        c = self.cfg
+        ids, rm = _c(ids, np.int32), _c(remap, np.int32)
+        table = _c(table, self.store)
+        hidden = _c(hidden, self.store).reshape(-1, c.hc_mult * c.hidden)
+        dy = _c(dy, self.store).reshape(-1, c.hc_mult * c.hidden)
+        tk = None if table_keys is None else _c(table_keys, np.int64)
+        hk = None if hidden_keys is None else _c(hidden_keys, np.int64)
+        yk = None if dy_keys is None else _c(dy_keys, np.int64)
+        args = [_c(a, self.store) for a in (w_kv, gamma_k, gamma_q, conv_w)]
+        pos = _c(positions, np.int64)
+        dh = np.empty((len(pos), c.hc_mult, c.hidden), np.float64)
+        de = np.empty((len(pos), self.emb_dim), np.float64) if want_de else None
+        trows, hrows, yrows = self._rows(table, tk), self._rows(hidden, hk), self._rows(dy, yk)
+        _ok(_load().orc_backward_at(ctypes.byref(c), _p(rm), len(rm), _p(ids), ctypes.byref(trows),
+                                    *[_p(a) for a in args], ctypes.byref(hrows), ctypes.byref(yrows), len(pos),
+                                    _p(pos), _p(dh), _p(de)), "orc_backward_at")
+        return dh, de
 
 
 def needed_positions(T: int, positions: np.ndarray, conv_kernel: int, dilation: int) -> np.ndarray:

@@ -392,6 +392,60 @@ out0:
   return rc;
 }
 
+/* Value fusion and gate backward of one token (the steps "value fusion",
+ * "gate" and "RMSNorm" of the gradients below): from dVg [hc][d] and the
+ * token's K/V (double [hc+1][d]), query row q [hc][d] (stored type), gates g
+ * and scores s [hc], writes dKV [hc+1][d] (dK of each branch, then dV) and
+ * d hidden [hc][d], and adds the token's terms to d_gk, d_gq [hc][d] when
+ * they are not NULL. */
+static void gate_backward_token(const orc_config *c, const double *kv, const void *q, const void *gamma_k,
+                                const void *gamma_q, const double *dvg, const double *g, const double *s,
+                                double *dkv, double *d_hidden, double *d_gk, double *d_gq) {
+  const int hc = c->hc_mult;
+  const int64_t d = c->hidden;
+  const double *V = kv + (int64_t)hc * d;
+  for (int64_t ch = 0; ch < d; ch++) {
+    double acc = 0.0;
+    for (int h = 0; h < hc; h++) acc += g[h] * dvg[(int64_t)h * d + ch];
+    dkv[(int64_t)hc * d + ch] = acc;
+  }
+  for (int h = 0; h < hc; h++) {
+    const double *Kv = kv + (int64_t)h * d;
+    const int64_t q0 = (int64_t)h * d;
+    double dg = 0.0, kk = 0.0, qq = 0.0;
+    for (int64_t ch = 0; ch < d; ch++) {
+      const double qv = ld(q, q0 + ch, c->dtype);
+      dg += dvg[q0 + ch] * V[ch];
+      kk += Kv[ch] * Kv[ch];
+      qq += qv * qv;
+    }
+    const double gv = g[h], sv = s[h];
+    const double da = dg * gv * (1.0 - gv);
+    const double ds = (sv != 0.0 && fabs(sv) >= c->gate_clamp) ? da / (2.0 * sqrt(fabs(sv))) : 0.0;
+    const double rk = 1.0 / sqrt(kk / (double)d + c->norm_eps);
+    const double rq = 1.0 / sqrt(qq / (double)d + c->norm_eps);
+    const double sd = sqrt((double)d);
+    double A = 0.0, B = 0.0;
+    for (int64_t ch = 0; ch < d; ch++) {
+      const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
+      const double qv = ld(q, q0 + ch, c->dtype);
+      const double u = Kv[ch] * rk * gk, v = qv * rq * gq;
+      const double du = ds * v / sd, dv = ds * u / sd;
+      A += du * gk * Kv[ch];
+      B += dv * gq * qv;
+      if (d_gk) d_gk[(int64_t)h * d + ch] += du * Kv[ch] * rk;
+      if (d_gq) d_gq[(int64_t)h * d + ch] += dv * qv * rq;
+    }
+    for (int64_t ch = 0; ch < d; ch++) {
+      const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
+      const double qv = ld(q, q0 + ch, c->dtype);
+      const double du = ds * qv * rq * gq / sd, dv = ds * Kv[ch] * rk * gk / sd;
+      dkv[(int64_t)h * d + ch] = rk * gk * du - rk * rk * rk * Kv[ch] * A / (double)d;
+      d_hidden[q0 + ch] = rq * gq * dv - rq * rq * rq * qv * B / (double)d;
+    }
+  }
+}
+
 /* Gradients of the module's output (the backward pass of a training step;
  * the pages train the module, walk-through 4.4).  Nothing here is on the
  * pages: these are the exact derivatives of the forward definitions above,
@@ -463,48 +517,9 @@ int orc_backward(const orc_config *c, const int32_t *remap, int32_t vocab, const
           dvg[(nn * hc + h) * d + ch] = acc;
         }
   /* value fusion and gate */
-  for (int64_t nn = 0; nn < n; nn++) {
-    for (int64_t ch = 0; ch < d; ch++) {
-      double acc = 0.0;
-      for (int h = 0; h < hc; h++) acc += g[nn * hc + h] * dvg[(nn * hc + h) * d + ch];
-      dkv[nn * O + (int64_t)hc * d + ch] = acc;
-    }
-    for (int h = 0; h < hc; h++) {
-      const double *Kv = kv + nn * O + (int64_t)h * d;
-      const int64_t q0 = (nn * hc + h) * d;
-      double dg = 0.0, kk = 0.0, qq = 0.0;
-      for (int64_t ch = 0; ch < d; ch++) {
-        const double q = ld(hidden, q0 + ch, c->dtype);
-        dg += dvg[q0 + ch] * kv[nn * O + (int64_t)hc * d + ch];
-        kk += Kv[ch] * Kv[ch];
-        qq += q * q;
-      }
-      const double gv = g[nn * hc + h], sv = s[nn * hc + h];
-      const double da = dg * gv * (1.0 - gv);
-      const double ds = (sv != 0.0 && fabs(sv) >= c->gate_clamp) ? da / (2.0 * sqrt(fabs(sv))) : 0.0;
-      const double rk = 1.0 / sqrt(kk / (double)d + c->norm_eps);
-      const double rq = 1.0 / sqrt(qq / (double)d + c->norm_eps);
-      const double sd = sqrt((double)d);
-      double A = 0.0, B = 0.0;
-      for (int64_t ch = 0; ch < d; ch++) {
-        const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
-        const double q = ld(hidden, q0 + ch, c->dtype);
-        const double u = Kv[ch] * rk * gk, v = q * rq * gq;
-        const double du = ds * v / sd, dv = ds * u / sd;
-        A += du * gk * Kv[ch];
-        B += dv * gq * q;
-        d_gk[(int64_t)h * d + ch] += du * Kv[ch] * rk;
-        d_gq[(int64_t)h * d + ch] += dv * q * rq;
-      }
-      for (int64_t ch = 0; ch < d; ch++) {
-        const double gk = ld(gamma_k, (int64_t)h * d + ch, c->dtype), gq = ld(gamma_q, (int64_t)h * d + ch, c->dtype);
-        const double q = ld(hidden, q0 + ch, c->dtype);
-        const double du = ds * q * rq * gq / sd, dv = ds * Kv[ch] * rk * gk / sd;
-        dkv[nn * O + (int64_t)h * d + ch] = rk * gk * du - rk * rk * rk * Kv[ch] * A / (double)d;
-        d_hidden[q0 + ch] = rq * gq * dv - rq * rq * rq * q * B / (double)d;
-      }
-    }
-  }
+  for (int64_t nn = 0; nn < n; nn++)
+    gate_backward_token(c, kv + nn * O, (const uint8_t *)hidden + nn * hc * d * esz, gamma_k, gamma_q,
+                        dvg + nn * hc * d, g + nn * hc, s + nn * hc, dkv + nn * O, d_hidden + nn * hc * d, d_gk, d_gq);
   /* projections */
   for (int64_t o = 0; o < O; o++)
     for (int64_t i = 0; i < E; i++) {
@@ -527,5 +542,75 @@ int orc_backward(const orc_config *c, const int32_t *remap, int32_t vocab, const
   rc = ORC_OK;
 out:
   free(idx); free(e); free(kv); free(s); free(g); free(dvg); free(dkv); free(de);
+  return rc;
+}
+
+/* The gradients that belong to single positions, at chosen flat positions
+ * pos[i] = b*T + t, by the same steps as orc_backward: d_hidden [n_pos][hc][d]
+ * and, when de is not NULL, de [n_pos][E], the gradient of the gathered
+ * vector e at that position (table row r of head h receives the sum of head
+ * h's slice of de over the positions whose index is r).  A position reads e,
+ * K, V, g and hidden at itself only, and dy at itself and D, 2D, ...,
+ * (K-1)D positions later in its sequence: hidden and dy are row sources keyed
+ * by flat position, one [hc][d] row each in the stored type. */
+int orc_backward_at(const orc_config *c, const int32_t *remap, int32_t vocab, const int32_t *ids,
+                    const orc_rows *table, const void *w_kv, const void *gamma_k, const void *gamma_q,
+                    const void *conv_w, const orc_rows *hidden, const orc_rows *dy, int64_t n_pos,
+                    const int64_t *pos, double *d_hidden, double *de) {
+  if (check(c)) return ORC_EINVAL;
+  const int64_t T = c->seqlen, n = (int64_t)c->batch * T;
+  const int H = n_heads(c), hc = c->hc_mult, K = c->conv_kernel, D = c->conv_dilation;
+  const int64_t d = c->hidden, E = (int64_t)H * c->head_dim, O = (int64_t)(hc + 1) * d;
+  const int64_t esz = c->dtype == 0 ? 4 : 2;
+  for (int64_t i = 0; i < n_pos; i++)
+    if (pos[i] < 0 || pos[i] >= n) return ORC_EINVAL;
+  if (n_pos == 0) return ORC_OK;
+
+  int64_t *idx = malloc(sizeof(int64_t) * n * H);
+  void *e = malloc(esz * E);
+  double *kv = malloc(sizeof(double) * O), *dkv = malloc(sizeof(double) * O);
+  double *dvg = malloc(sizeof(double) * hc * d), *g = malloc(sizeof(double) * hc), *s = malloc(sizeof(double) * hc);
+  int rc = ORC_ENOMEM;
+  if (!idx || !e || !kv || !dkv || !dvg || !g || !s) goto out;
+  rc = orc_hash(c, remap, vocab, ids, NULL, idx);
+  if (rc) goto out;
+  orc_config one = *c;
+  one.batch = 1;
+  one.seqlen = 1;
+  for (int64_t i = 0; i < n_pos; i++) {
+    const int64_t p = pos[i], t = p % T;
+    /* forward quantities at the position */
+    rc = orc_gather(&one, table, idx + p * H, 1, e);
+    if (!rc) rc = orc_project(&one, w_kv, e, 1, kv);
+    if (rc) goto out;
+    const void *q = row_ptr(hidden, p, esz * hc * d);
+    if (!q) { rc = ORC_EMISSING; goto out; }
+    rc = orc_gate(&one, gamma_k, gamma_q, kv, q, 1, s, g);
+    if (rc) goto out;
+    /* conv + residual: dy at the position and at the K-1 positions its Vg feeds */
+    const void *dy0 = row_ptr(dy, p, esz * hc * d);
+    if (!dy0) { rc = ORC_EMISSING; goto out; }
+    for (int64_t k = 0; k < hc * d; k++) dvg[k] = ld(dy0, k, c->dtype);
+    for (int j = 0; j < K; j++) {
+      const int64_t ahead = t + (int64_t)(K - 1 - j) * D;
+      if (ahead >= T) continue;
+      const void *dyr = row_ptr(dy, p + (ahead - t), esz * hc * d);
+      if (!dyr) { rc = ORC_EMISSING; goto out; }
+      for (int h = 0; h < hc; h++)
+        for (int64_t ch = 0; ch < d; ch++)
+          dvg[(int64_t)h * d + ch] +=
+              ld(conv_w, ((int64_t)h * d + ch) * K + j, c->dtype) * ld(dyr, (int64_t)h * d + ch, c->dtype);
+    }
+    gate_backward_token(c, kv, q, gamma_k, gamma_q, dvg, g, s, dkv, d_hidden + i * hc * d, NULL, NULL);
+    if (de)
+      for (int64_t k = 0; k < E; k++) {
+        double acc = 0.0;
+        for (int64_t o = 0; o < O; o++) acc += dkv[o] * ld(w_kv, o * E + k, c->dtype);
+        de[i * E + k] = acc;
+      }
+  }
+  rc = ORC_OK;
+out:
+  free(idx); free(e); free(kv); free(dkv); free(dvg); free(g); free(s);
   return rc;
 }

@@ -110,3 +110,41 @@ def test_backward_zero_hidden_closed_form():
     hc, d = w.hc_mult, w.hidden
     assert np.all(got["d_w_kv"][: hc * d] == 0)          # key rows get nothing
     assert np.abs(got["d_w_kv"][hc * d:]).max() > 0       # value rows do
+
+
+@pytest.mark.parametrize("name,over", [("tiny_fp32", {}), ("tiny_fp32", dict(hc_mult=3, batch=2, seqlen=40)),
+                                       ("b4_t1024", dict(batch=2, seqlen=24, hidden=64, head_dim=8,
+                                                         heads_per_order=2, prime_base=101))])
+def test_backward_at_matches_dense_backward(name, over):
+    """orc_backward_at at every position (sparse rows, each keyed by flat
+    position) gives the dense backward's d hidden, and its de summed by
+    table row gives the dense d_table (both pinned above against autograd)."""
+    w = S.WORKLOADS[name].replace(**over)
+    inp = S.Inputs(w)
+    o = orc.Oracle.from_workload(w, inp, batch=w.batch, seqlen=w.seqlen)
+    B, T = w.batch, w.seqlen
+    b, t = np.divmod(np.arange(B * T), T)
+    hidden, dy = inp.hidden_at(b, t), inp.dy_at(b, t)
+    table = inp.table()
+    args = dict(ids=inp.ids, remap=inp.remap, table=table, w_kv=inp.wkv(), gamma_k=inp.gamma_k(),
+                gamma_q=inp.gamma_q(), conv_w=inp.conv_w())
+    dy64 = (dy.astype(np.float32) if w.dtype == "f32" else S.bf16_bits_to_f32(dy)).astype(np.float64)
+    dense = o.backward(hidden=hidden.reshape(B, T, w.hc_mult, w.hidden), dy=dy64.reshape(B, T, w.hc_mult, w.hidden),
+                       **args)
+    # positions in a shuffled order, hidden/dy as sparse rows keyed by position
+    pos = np.random.default_rng(0).permutation(B * T)
+    keys = np.arange(B * T, dtype=np.int64)
+    dh, de = o.backward_at(hidden=hidden, dy=dy, positions=pos, hidden_keys=keys, dy_keys=keys, **args)
+    ref_dh = dense["d_hidden"].reshape(B * T, w.hc_mult, w.hidden)[pos]
+    assert np.abs(dh - ref_dh).max() <= 1e-12 * np.abs(ref_dh).max()
+    idx = o.hash(inp.ids, remap=inp.remap).reshape(B * T, -1)[pos]
+    off = np.concatenate([[0], np.cumsum(inp.primes)[:-1]])
+    acc = np.zeros_like(dense["d_table"])
+    H, Dh = idx.shape[1], w.head_dim
+    for h in range(H):
+        np.add.at(acc, idx[:, h] + off[h], de[:, h * Dh:(h + 1) * Dh])
+    assert np.abs(acc - dense["d_table"]).max() <= 1e-12 * np.abs(dense["d_table"]).max()
+    # missing rows are reported, not read
+    with pytest.raises(orc.OracleError):
+        o.backward_at(hidden=hidden[:5], dy=dy[:5], positions=pos[:1], hidden_keys=keys[:5], dy_keys=keys[:5],
+                      **args)

@@ -391,6 +391,34 @@ def bench_train(args, w):
     print(json.dumps(res))
 
 
+def bench_vocab(args, w):
+    """Compressed token ids (walk-through 2.2-1, 4.1): the host builder of the
+    remap table on a synthetic vocabulary of the workload's size, best of 5;
+    the oracle's builder timed once beside it as the CPU baseline."""
+    from engram_synth.vocab import synthetic_vocab
+    from hashed_gram_conditional_amd.compressed_vocab import build_remap
+
+    texts = synthetic_vocab(w.seed, w.vocab)
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        remap, n = build_remap(texts)
+        times.append(time.perf_counter() - t0)
+    best = min(times)
+    res = {"mode": "vocab", "metric": "compressed-id table build, tokens/s (host)", "value": round(len(texts) / best, 1),
+           "unit": "tokens/s", "seconds": round(best, 4), "vocab": len(texts), "compressed": int(n),
+           "reduction": round(1 - n / len(texts), 4), "data": "synthetic vocabulary", "config": {"workload": w.name}}
+    if not args.no_cpu_baseline:
+        from oracle.compressed_vocab import compressed_ids
+
+        t0 = time.perf_counter()
+        compressed_ids(texts)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(len(texts) / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole {len(texts)}-token vocabulary"}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +433,8 @@ def main():
                          "control without the cache reuse of frequent n-grams)")
     ap.add_argument("--offload", action="store_true",
                     help="tables in host memory: measure the prefetch flow against HBM-resident tables")
+    ap.add_argument("--vocab", action="store_true",
+                    help="host build of the compressed-id table from a synthetic vocabulary of the workload's size")
     ap.add_argument("--train", action="store_true",
                     help="forward + backward (gradients of the tables and weights) per step")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -428,6 +458,8 @@ def main():
         return bench_offload(args, w)
     if args.train:
         return bench_train(args, w)
+    if args.vocab:
+        return bench_vocab(args, w)
     if w.decode_prompt:
         return bench_decode(args, w)
     inp = S.Inputs(w)

@@ -105,6 +105,30 @@ def test_hash_negative_multipliers_and_pad(eg):
     assert np.array_equal(got.cpu().numpy(), o.hash(ids))
 
 
+def test_hash_with_a_compressed_vocabulary(eg):
+    """The remap built from token texts (compressed ids: NFKC, lower case,
+    accents removed, equal keys merged) drives the hash: bit-exact against the
+    oracle's hash with the oracle's own compressed ids."""
+    import oracle as orc
+    from engram_synth.vocab import synthetic_vocab
+    from hashed_gram_conditional_amd.compressed_vocab import build_remap
+    from oracle.compressed_vocab import compressed_ids
+
+    c = case("b4_t1024")
+    texts = synthetic_vocab(c.w.seed, c.w.vocab)
+    remap, n = build_remap(texts)
+    ref_remap, n_ref = compressed_ids(texts)
+    assert n == n_ref
+    d = c.dev
+    p = eg.Params(remap=torch.from_numpy(remap).cuda(), tables=d["tables"], w_kv=d["w_kv"], gamma_k=d["gamma_k"],
+                  gamma_q=d["gamma_q"], conv_w=d["conv_w"])
+    got = eg.engram_hash(c.cfg(), p, d["ids"])
+    sync()
+    o = orc.Oracle.from_workload(c.w, c.inp, batch=c.B, seqlen=c.T)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64),
+                          o.hash(c.inp.ids, remap=np.asarray(ref_remap, dtype=np.int32)))
+
+
 # ------------------------------------------------------------------ gather
 @pytest.mark.parametrize("name", ["tiny_fp32", "b4_t1024", "b8_t4096"])
 def test_gather_bit_exact(eg, name):

@@ -24,22 +24,23 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 
 
-def kernel_model(w, N):
+def kernel_model(w, N, split=False):
     """Algorithmic work per launch of each kernel: (bound, amount, unit).
     Bytes count what the method must move (rows, ids, activations, outputs),
-    not re-reads; the GEMMs count their multiply-adds as 2 flops."""
+    not re-reads; the GEMMs count their multiply-adds as 2 flops.  `split`:
+    the fused GEMM covers the key channels and project_value_gemm the value
+    channels."""
     s = 2 if w.dtype == "bf16" else 4
     E, d, hc = w.emb_dim, w.hidden, w.hc_mult
-    # partial sums per (token, branch) of the fused GEMM: d over its channel tile
-    # (256 when the GEMM has at least 4 tiles of 256x256 per CU, else 128)
-    tile = 256 if ((N + 255) // 256) * (((hc + 1) * d + 255) // 256) >= 4 * 256 else 128
     flops = 2.0 * N * E * (hc + 1) * d
     return {
         "hash_gather": ("hbm", N * (4 + 2 * E * s), "B"),
         "project_gemm": ("mfma" if w.dtype == "bf16" else "alu", flops, "FLOP"),
-        "project_gate_gemm": ("mfma", flops, "FLOP"),
+        "project_gate_gemm": ("mfma", 2.0 * N * E * hc * d if split else flops, "FLOP"),
+        "project_value_gemm": ("mfma", 2.0 * N * E * d, "FLOP"),
         "gate": ("hbm", N * (2 * hc * d * s + 4 * hc), "B"),
-        "gate_finalize": ("hbm", N * hc * (16 * (d // tile) + 4), "B"),
+        # the fused GEMM's partial sums: one float4 per 128 channels of each (token, branch)
+        "gate_finalize": ("hbm", N * hc * (16 * (d // 128) + 4), "B"),
         "short_conv": ("hbm", N * (d * s + 4 * hc + hc * d * s), "B"),
         "advance_state": ("hbm", 0, "B"),
     }
@@ -510,7 +511,7 @@ def main():
         hip.destroy(e)
 
     ms_per_step = dt * 1e3 / args.steps
-    model = kernel_model(w, N)
+    model = kernel_model(w, N, split="project_value_gemm" in names)
     kernels = []
     for name, ms in zip(names, per_kernel_ms):
         bound, amount, unit = model[name]

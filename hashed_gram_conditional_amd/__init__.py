@@ -494,6 +494,12 @@ def backward_saved(cfg: EngramConfig, p: Params, hidden, dy, workspace, grads=No
 
 
 def kernel_names(cfg: EngramConfig, with_state: bool = False):
+    """Names of the kernels engram_forward launches for cfg, in launch order."""
     lib = load()
-    n = 5 if with_state else 4
-    return [lib.engram_forward_kernel_name(ctypes.byref(cfg), i).decode() for i in range(n)]
+    names = []
+    while True:
+        nm = lib.engram_forward_kernel_name(ctypes.byref(cfg), len(names))
+        if nm is None:
+            break
+        names.append(nm.decode())
+    return names if with_state else [n for n in names if n != "advance_state"]

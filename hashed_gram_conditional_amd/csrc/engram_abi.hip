@@ -116,19 +116,21 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // engram_forward runs the fused path (projection GEMM with the gate sums in
 // its epilogue, then a small finalize kernel) when the weights are bf16 and the
-// GEMM's channel tile divides the hidden size; otherwise the projections are
-// stored and a separate gate kernel reads them back.
-int fused_tile(const engram_config* c) {
-  if (c->dtype != ENGRAM_BF16) return 0;
-  const int64_t N = (int64_t)c->batch * c->seqlen;
-  return gemm_gate_tile_n(N, (c->hc_mult + 1) * c->hidden, (int)emb_dim(c), c->hidden);
+// GEMM's channel tile divides the hidden size -- for some shapes with the value
+// channels as a plain GEMM after the key channels (gemm_gate_plan); otherwise
+// the projections are stored and a separate gate kernel reads them back.
+GatePlan gate_plan(const engram_config* c) {
+  if (c->dtype != ENGRAM_BF16) return GatePlan{0, false};
+  return gemm_gate_plan((int64_t)c->batch * c->seqlen, c->hc_mult, c->hidden);
 }
+
+int fused_tile(const engram_config* c) { return gate_plan(c).tile; }
 
 struct Workspace {
   void* e;         // [N][E]
   void* kv;        // unfused: [N][hc+1][d]
   void* v;         // fused: [N][d]
-  float4* part;    // fused: [N][hc][d / tile]
+  float4* part;    // fused: [N][hc][d / 128]
   float* g;        // [N][hc]
   size_t bytes;
 };
@@ -146,7 +148,7 @@ Workspace carve(const engram_config* c, void* base) {
   w.e = take((size_t)N * emb_dim(c) * esize(c));
   if (tile) {
     w.v = take((size_t)N * c->hidden * esize(c));
-    w.part = (float4*)take((size_t)N * c->hc_mult * (c->hidden / tile) * sizeof(float4));
+    w.part = (float4*)take((size_t)N * c->hc_mult * (c->hidden / 128) * sizeof(float4));
   } else {
     w.kv = take((size_t)N * (c->hc_mult + 1) * c->hidden * esize(c));
   }
@@ -214,6 +216,8 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
 const char* const kForwardKernels[] = {"hash_gather", "project_gemm", "gate", "short_conv", "advance_state"};
 const char* const kFusedKernels[] = {"hash_gather", "project_gate_gemm", "gate_finalize", "short_conv",
                                      "advance_state"};
+const char* const kSplitKernels[] = {"hash_gather", "project_gate_gemm", "project_value_gemm", "gate_finalize",
+                                     "short_conv", "advance_state"};
 
 GatherArgs gather_args(const engram_config* c, const engram_params* p, const int32_t* ids, const engram_state* st) {
   GatherArgs a;
@@ -305,7 +309,8 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   if ((rc = gathered ? check_params_no_tables(c, p) : check_params(c, p))) return rc;
   if ((rc = check_state(c, st))) return rc;
   const int64_t N = (int64_t)c->batch * c->seqlen;
-  const int nk = (st ? 5 : 4) - (gathered ? 1 : 0);
+  const GatePlan plan = gate_plan(c);
+  const int nk = (st ? 5 : 4) - (gathered ? 1 : 0) + (plan.split ? 1 : 0);
   if (n_kernels) *n_kernels = N == 0 ? 0 : nk;
   if (N == 0) return ENGRAM_OK;
   if ((!gathered || st != nullptr) && ids == nullptr) return ENGRAM_EINVAL;
@@ -343,14 +348,22 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
     gg.partials = w.part;
     gg.hc = c->hc_mult;
     gg.d = c->hidden;
+    gg.tile_n = plan.tile;
+    if (plan.split) gg.g.N = c->hc_mult * c->hidden;   // key channels only
     if ((e = tm.before()) || (e = launch_gemm_gate_bf16(gg, s)) || (e = tm.after())) return hip_status(e);
+    if (plan.split) {   // value channels: V = W_v e into the workspace
+      GemmArgs gv = gemm_args(c, p, e_rows, w.v);
+      gv.B = (const uint8_t*)p->w_kv + (int64_t)c->hc_mult * c->hidden * emb_dim(c) * esize(c);
+      gv.N = c->hidden;
+      if ((e = tm.before()) || (e = launch_gemm_bf16(gv, s)) || (e = tm.after())) return hip_status(e);
+    }
     GateFinalizeArgs gf;
     gf.partials = w.part;
     gf.g_out = w.g;
     gf.n_tok = (int32_t)N;
     gf.hc = c->hc_mult;
     gf.d = c->hidden;
-    gf.n_part = c->hidden / fused_tile(c);
+    gf.n_part = c->hidden / 128;   // one partial per 128 channels, whatever the tile
     gf.eps = c->norm_eps;
     gf.clamp = c->gate_clamp;
     gf.inv_sqrt_d = (float)(1.0 / sqrt((double)c->hidden));
@@ -761,8 +774,11 @@ engram_status engram_gather_host(const engram_config* cfg, const void* tables, c
 }
 
 const char* engram_forward_kernel_name(const engram_config* cfg, int32_t i) {
-  if (validate(cfg) || i < 0 || i >= 5) return nullptr;
-  return fused_tile(cfg) ? kFusedKernels[i] : kForwardKernels[i];
+  if (validate(cfg) || i < 0) return nullptr;
+  const GatePlan plan = gate_plan(cfg);
+  if (plan.split) return i < 6 ? kSplitKernels[i] : nullptr;
+  if (i >= 5) return nullptr;
+  return plan.tile ? kFusedKernels[i] : kForwardKernels[i];
 }
 
 const char* engram_status_string(engram_status s) {

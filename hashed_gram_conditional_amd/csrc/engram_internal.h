@@ -101,13 +101,19 @@ struct GemmGateArgs {
   const void* gamma_k;    // [hc][d]
   const void* gamma_q;    // [hc][d]
   void* v_out;            // [M][d]
-  float4* partials;       // [M][hc][n_part] (x = sum K^2, y = sum Q^2, z = sum K gk gq Q)
+  float4* partials;       // [M][hc][d/128]: per 128 channels x = sum K^2, y = sum Q^2, z = sum K gk gq Q
   int32_t hc, d;
+  int32_t tile_n;         // channel tile: 256 or 128 (from gemm_gate_plan)
 };
 
-// channel tile width of the fused GEMM for this shape (the partials per
-// (token, branch) are d / width), or 0 when the fused path does not apply
-int gemm_gate_tile_n(int64_t M, int N, int K, int d);
+// How the fused projection runs for M tokens: `tile` is its channel tile (0:
+// the fused path does not apply); `split`: the gate GEMM covers the key
+// channels only and the value channels run as a plain GEMM after it.
+struct GatePlan {
+  int tile;
+  bool split;
+};
+GatePlan gemm_gate_plan(int64_t M, int hc, int d);
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s);
 
 // g[n][h] from the partial sums of the fused GEMM

@@ -43,17 +43,23 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, bool bf16, float
   }
 }
 
+// 8 outputs of the module, stored non-temporally: the output is written once
+// and not read again here, so it should not evict the table rows that the
+// next call's gather finds in the last-level cache (B=8 T=4096: gather 37 ->
+// 30 us; B=4 T=1024: conv 16.4 -> 14.7 us).
 __device__ __forceinline__ void store8(void* p, int64_t i, bool bf16, const float* v) {
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
   if (bf16) {
-    uint4 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-    *(uint4*)((uint16_t*)p + i) = u;
+    const w4 u = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                  (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16),
+                  (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16),
+                  (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16)};
+    __builtin_nontemporal_store(u, (w4*)((uint16_t*)p + i));
   } else {
-    *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
-    *(float4*)((float*)p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    const w4 a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    const w4 b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+    __builtin_nontemporal_store(a, (w4*)((float*)p + i));
+    __builtin_nontemporal_store(b, (w4*)((float*)p + i + 4));
   }
 }
 

@@ -22,6 +22,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <algorithm>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -119,8 +121,8 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // GATE = false: the tile is stored to C (bf16).
 // GATE = true (fused gate): a tile of branch h's key channels is not stored;
 // its epilogue reads the matching tile of the hidden state Q (the query of
-// branch h) and the two RMSNorm scales, and writes per token the partial sums
-// over its BN channels of K^2, Q^2 and K gk gq Q -- everything the gate needs
+// branch h) and the two RMSNorm scales, and writes per token and 128 channels
+// the partial sums of K^2, Q^2 and K gk gq Q -- everything the gate needs
 // from K (formula sheet, kwkr.cn/news/37585, section 2.2 step 1: the gate is
 // the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
 // square).  Value tiles are stored to v_out.  Writing K and reading it back
@@ -446,18 +448,28 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     const int c0 = (int)(n0 - (int64_t)h * d);
     const uint16_t* gks = reinterpret_cast<const uint16_t*>(&smem[kGammaBase]) + wn * (BN / WN) + 4 * lhalf;
     const uint16_t* gqs = reinterpret_cast<const uint16_t*>(&smem[kGammaBase + 64]) + wn * (BN / WN) + 4 * lhalf;
+    // Partial sums are per 128 channels, whatever the tile: a wave of a
+    // 128-wide tile covers 64 channels and the two waves of a row add theirs
+    // in LDS; a wave of a 256-wide tile covers 128 channels, kept as two
+    // 64-channel sums (kHalves) added once.  Either way each 128-channel sum is
+    // (sum of the first 64) + (sum of the next 64), every term in the same
+    // order, so the gates do not depend on the tile the call was planned with.
+    constexpr int kHalves = BN / WN == 128 ? 2 : 1;
+    static_assert(BN / WN == 128 || BN / WN == 64, "fused gate epilogue: 64 or 128 channels per wave");
     const uint16_t* q_rows[TM];
-    float kk[TM], qq[TM], kq[TM];
+    float kk[kHalves][TM], qq[kHalves][TM], kq[kHalves][TM];
 #pragma unroll
     for (int j = 0; j < TM; j++) {
       q_rows[j] = q_row(j);
-      kk[j] = qq[j] = kq[j] = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < kHalves; hf++) kk[hf][j] = qq[hf][j] = kq[hf][j] = 0.f;
     }
     // per token: sums over this lane's runs of 4 channels
 #pragma unroll
     for (int i = 0; i < TN; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
+        const int hf = kHalves == 2 && i >= TN / 2 ? 1 : 0;
         float x[4], y[4], g[4];
         load4(gks + 32 * i + 8 * q, x);
         load4(gqs + 32 * i + 8 * q, y);
@@ -494,18 +506,34 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const float k = acc[i][j][4 * q + e];
-            kk[j] = fmaf(k, k, kk[j]);
-            qq[j] = fmaf(qv[e], qv[e], qq[j]);
-            kq[j] = fmaf(k * g[e], qv[e], kq[j]);
+            kk[hf][j] = fmaf(k, k, kk[hf][j]);
+            qq[hf][j] = fmaf(qv[e], qv[e], qq[hf][j]);
+            kq[hf][j] = fmaf(k * g[e], qv[e], kq[hf][j]);
           }
         }
       }
 #pragma unroll
-    for (int j = 0; j < TM; j++) {
-      // lanes l and l+32 hold the other half of the wave's channels of the same token
-      kk[j] += __shfl_xor(kk[j], 32, 64);
-      qq[j] += __shfl_xor(qq[j], 32, 64);
-      kq[j] += __shfl_xor(kq[j], 32, 64);
+    for (int hf = 0; hf < kHalves; hf++)
+#pragma unroll
+      for (int j = 0; j < TM; j++) {
+        // lanes l and l+32 hold the other half of each 8-channel run of the same token
+        kk[hf][j] += __shfl_xor(kk[hf][j], 32, 64);
+        qq[hf][j] += __shfl_xor(qq[hf][j], 32, 64);
+        kq[hf][j] += __shfl_xor(kq[hf][j], 32, 64);
+      }
+    const int n_part = d / 128;
+    if constexpr (kHalves == 2) {
+      if (lhalf == 0) {
+        const int part = (c0 + wn * 128) / 128;
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+          const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
+          if (m < a.M)
+            ga.partials[(m * hc + h) * n_part + part] =
+                make_float4(kk[0][j] + kk[1][j], qq[0][j] + qq[1][j], kq[0][j] + kq[1][j], 0.f);
+        }
+      }
+      return;
     }
     // the WN waves of a token row meet in LDS; the operand stages are free now
     __syncthreads();
@@ -513,10 +541,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     if (lhalf == 0)
 #pragma unroll
       for (int j = 0; j < TM; j++)
-        red[((wn * WM + wm) * TM + j) * 32 + lrow] = make_float4(kk[j], qq[j], kq[j], 0.f);
+        red[((wn * WM + wm) * TM + j) * 32 + lrow] = make_float4(kk[0][j], qq[0][j], kq[0][j], 0.f);
     __syncthreads();
     if (wn == 0 && lhalf == 0) {
-      const int n_part = d / BN, part = c0 / BN;
+      const int part = c0 / 128;
 #pragma unroll
       for (int j = 0; j < TM; j++) {
         const int64_t m = m0 + wm * (BM / WM) + j * 32 + lrow;
@@ -535,24 +563,29 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   }
 }
 
-// g from the fused GEMM's partial sums: one thread per (token, branch); the
-// partials are read 8 at a time with independent loads.
-__global__ void __launch_bounds__(64) k_gate_finalize(GateFinalizeArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (i >= (int64_t)a.n_tok * a.hc) return;
-  const float4* p = a.partials + i * a.n_part;
+// g from the fused GEMM's partial sums: 8 lanes per (token, branch), lane l
+// adding partials l, l+8, ... (consecutive lanes read consecutive 16-byte
+// partials), then the 8 lane sums combined by xor shuffles in a fixed order.
+__global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int l = threadIdx.x & 7;
+  const bool ok = i < (int64_t)a.n_tok * a.hc;
+  const float4* p = a.partials + (ok ? i : 0) * a.n_part;
   float kk = 0.f, qq = 0.f, kq = 0.f;
-  for (int t0 = 0; t0 < a.n_part; t0 += 8) {
-    float4 v[8];
-#pragma unroll
-    for (int t = 0; t < 8; t++) v[t] = t0 + t < a.n_part ? p[t0 + t] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-      kk += v[t].x;
-      qq += v[t].y;
-      kq += v[t].z;
+  if (ok)
+    for (int t = l; t < a.n_part; t += 8) {
+      const float4 v = p[t];
+      kk += v.x;
+      qq += v.y;
+      kq += v.z;
     }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    kk += __shfl_xor(kk, o, 64);
+    qq += __shfl_xor(qq, o, 64);
+    kq += __shfl_xor(kq, o, 64);
   }
+  if (!ok || l != 0) return;
   const float inv_d = 1.f / (float)a.d;
   const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
   const float rq = 1.f / sqrtf(qq * inv_d + a.eps);
@@ -662,15 +695,40 @@ hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s) {
   return gemm_launch<128, 128, 2, 2, 2, false, true>(ga, s);
 }
 
-int gemm_gate_tile_n(int64_t M, int N, int K, int d) {
-  (void)K;
-  const int bn = pick_tile_n(M, N);
-  return (d % bn == 0) ? bn : 0;
+// Plan of the fused projection over M tokens and (hc+1) d channels, from a
+// model of its time in rounds of 256x256 tiles over the 256 CUs (a round of
+// 128x128 tiles, two per CU, costs ~0.34 of one: they move twice the operand
+// bytes per flop; measured on MI355X):
+//   one launch of 256x256 tiles (d % 256 == 0):   ceil(tiles / 256)
+//   one launch of 128x128 tiles (d % 128 == 0):   0.34 max(1, tiles / 256)
+//   split (d % 256 == 0): the key channels in 256x256 tiles with the gate
+//     epilogue, then the value channels as a plain GEMM in 128x128 tiles
+// B=4 T=1024 d=1024 hc=4: 320 large tiles are 2 rounds, 1280 small ones 1.7,
+// the split 1 + 0.34 (256 key tiles, then 256 value tiles).
+GatePlan gemm_gate_plan(int64_t M, int hc, int d) {
+  const int64_t mt256 = (M + 255) / 256, mt128 = (M + 127) / 128;
+  const double small = 0.34;
+  GatePlan best = {0, false};
+  double cost = 1e30;
+  if (d % 256 == 0) {
+    const double c = (double)((mt256 * ((int64_t)(hc + 1) * d / 256) + 255) / 256);
+    if (c < cost) best = {256, false}, cost = c;
+  }
+  if (d % 128 == 0) {
+    const double c = small * std::max(1.0, (double)(mt128 * ((int64_t)(hc + 1) * d / 128)) / 256.0);
+    if (c < cost) best = {128, false}, cost = c;
+  }
+  if (d % 256 == 0) {
+    const double c = (double)((mt256 * ((int64_t)hc * d / 256) + 255) / 256) +
+                     small * std::max(1.0, (double)(mt128 * (d / 128)) / 256.0);
+    if (c < 0.9 * cost) best = {256, true}, cost = c;
+  }
+  return best;
 }
 
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
   if (a.g.M == 0 || a.g.N == 0) return hipSuccess;
-  const int bn = gemm_gate_tile_n(a.g.M, a.g.N, a.g.K, a.d);
+  const int bn = a.tile_n;
   if (bn == 256) return gemm_launch<256, 256, 4, 2, 2, true>(a, s);
   if (bn == 128 && few_tiles(a.g.M, a.g.N)) return gemm_launch<128, 128, 2, 2, 4, true>(a, s);
   if (bn == 128) return gemm_launch<128, 128, 2, 2, 2, true>(a, s);
@@ -680,7 +738,7 @@ hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
 hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_tok * a.hc;
   if (n == 0) return hipSuccess;
-  k_gate_finalize<<<(unsigned)((n + 63) / 64), 64, 0, s>>>(a);
+  k_gate_finalize<<<(unsigned)((n * 8 + 255) / 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -251,11 +251,13 @@ def test_forward_within_tolerance(eg, name, n):
     (dict(batch=2, seqlen=100, hidden=200, hc_mult=3), False),   # d % 128 != 0: stored projections + gate kernel
     (dict(batch=3, seqlen=77, hidden=256, hc_mult=2), True),     # fused GEMM with a ragged token count
     (dict(batch=1, seqlen=300, hidden=384, hc_mult=1, orders=[2, 3, 4], conv_dilation=4), True),
+    (dict(batch=2, seqlen=2000), True),   # key channels 256-wide, then the value channels as a plain GEMM
 ])
 def test_forward_paths_on_ragged_shapes(eg, over, fused):
     c = case("b4_t1024", **over)
     names = eg.kernel_names(c.cfg())
     assert (names[1] == "project_gate_gemm") == fused, names
+    assert ("project_value_gemm" in names) == (c.B * c.T == 4000), names
     y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
     sync()
     N = c.B * c.T

@@ -72,7 +72,15 @@ def _run(eg, c, hid, seed, grads=None):
 
 CASES = [("tiny_fp32", {}),
          ("b4_t1024", dict(batch=2, seqlen=96, prime_base=4001)),
-         ("b4_t1024", dict(batch=1, seqlen=77, prime_base=4001, sigma_conv=0.5, sigma_gamma=0.5))]
+         ("b4_t1024", dict(batch=1, seqlen=77, prime_base=4001, sigma_conv=0.5, sigma_gamma=0.5)),
+         # 3 branches, d = 200 (25 channel groups), conv of 3 taps at dilation 2
+         ("b4_t1024", dict(batch=2, seqlen=50, prime_base=4001, hidden=200, hc_mult=3, conv_kernel=3,
+                           conv_dilation=2)),
+         # 2 taps at dilation 1, fp32 storage
+         ("tiny_fp32", dict(batch=3, seqlen=41, hc_mult=2, conv_kernel=2, conv_dilation=1)),
+         # the largest conv (8 taps), d = 64
+         ("b4_t1024", dict(batch=1, seqlen=70, prime_base=4001, hidden=64, hc_mult=2, conv_kernel=8,
+                           conv_dilation=1))]
 
 
 @pytest.mark.parametrize("name,over", CASES)

@@ -94,7 +94,8 @@ class EngramConfig(ctypes.Structure):
 
     @property
     def ring_len(self) -> int:
-        return (self.conv_kernel - 1) * self.conv_dilation
+        """Positions the value and gate rings of a state keep: the conv's history plus one."""
+        return (self.conv_kernel - 1) * self.conv_dilation + 1
 
 
 class _Params(ctypes.Structure):
@@ -140,7 +141,7 @@ def load():
         lib.engram_backward_saved.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_int32)]
-        lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32]
+        lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
         lib.engram_forward_kernel_name.restype = ctypes.c_char_p
         lib.engram_status_string.argtypes = [I]
         lib.engram_status_string.restype = ctypes.c_char_p
@@ -498,8 +499,8 @@ def kernel_names(cfg: EngramConfig, with_state: bool = False):
     lib = load()
     names = []
     while True:
-        nm = lib.engram_forward_kernel_name(ctypes.byref(cfg), len(names))
+        nm = lib.engram_forward_kernel_name(ctypes.byref(cfg), int(with_state), len(names))
         if nm is None:
             break
         names.append(nm.decode())
-    return names if with_state else [n for n in names if n != "advance_state"]
+    return names

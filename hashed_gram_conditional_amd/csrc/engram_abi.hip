@@ -19,7 +19,10 @@ int max_order(const engram_config* c) { return c->orders[c->n_orders - 1]; }
 int n_heads(const engram_config* c) { return c->n_orders * c->heads_per_order; }
 int64_t emb_dim(const engram_config* c) { return (int64_t)n_heads(c) * c->head_dim; }
 int64_t esize(const engram_config* c) { return c->dtype == ENGRAM_BF16 ? 2 : 4; }
-int ring_len(const engram_config* c) { return (c->conv_kernel - 1) * c->conv_dilation; }
+// Positions the value and gate rings keep: the conv's history (K-1) D plus
+// one, so that a decode step's new position never takes a slot the history
+// reads (the decode tail writes the ring while other workgroups read it).
+int ring_len(const engram_config* c) { return (c->conv_kernel - 1) * c->conv_dilation + 1; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -132,6 +135,7 @@ struct Workspace {
   void* v;         // fused: [N][d]
   float4* part;    // fused: [N][hc][d / 128]
   float* g;        // [N][hc]
+  int64_t* past;   // [B]: n_past before the call (decode steps with a state)
   size_t bytes;
 };
 
@@ -153,6 +157,7 @@ Workspace carve(const engram_config* c, void* base) {
     w.kv = take((size_t)N * (c->hc_mult + 1) * c->hidden * esize(c));
   }
   w.g = (float*)take((size_t)N * c->hc_mult * sizeof(float));
+  w.past = (int64_t*)take((size_t)c->batch * sizeof(int64_t));
   w.bytes = off;
   return w;
 }
@@ -218,6 +223,15 @@ const char* const kFusedKernels[] = {"hash_gather", "project_gate_gemm", "gate_f
                                      "advance_state"};
 const char* const kSplitKernels[] = {"hash_gather", "project_gate_gemm", "project_value_gemm", "gate_finalize",
                                      "short_conv", "advance_state"};
+const char* const kDecodeKernels[] = {"hash_gather", "project_gate_gemm", "decode_tail"};
+
+// A decode step (T = 1) with a state on the fused, unsplit projection ends in
+// one kernel (k_decode_tail) instead of gate_finalize, short_conv and
+// advance_state.
+bool decode_tail_path(const engram_config* c, bool with_state, bool gathered) {
+  const GatePlan p = gate_plan(c);
+  return with_state && !gathered && c->seqlen == 1 && p.tile && !p.split;
+}
 
 GatherArgs gather_args(const engram_config* c, const engram_params* p, const int32_t* ids, const engram_state* st) {
   GatherArgs a;
@@ -310,7 +324,8 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   if ((rc = check_state(c, st))) return rc;
   const int64_t N = (int64_t)c->batch * c->seqlen;
   const GatePlan plan = gate_plan(c);
-  const int nk = (st ? 5 : 4) - (gathered ? 1 : 0) + (plan.split ? 1 : 0);
+  const bool tail = decode_tail_path(c, st != nullptr, gathered);
+  const int nk = tail ? 3 : (st ? 5 : 4) - (gathered ? 1 : 0) + (plan.split ? 1 : 0);
   if (n_kernels) *n_kernels = N == 0 ? 0 : nk;
   if (N == 0) return ENGRAM_OK;
   if ((!gathered || st != nullptr) && ids == nullptr) return ENGRAM_EINVAL;
@@ -330,6 +345,7 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   if (!gathered) {
     GatherArgs ga = gather_args(c, p, ids, st);
     ga.e_out = (uint8_t*)w.e;
+    if (tail) ga.past_out = w.past;
     const int cap = gather_grid_cap(p->tables);
     if ((e = tm.before()) || (e = launch_hash_gather(hc, ga, true, s, cap)) || (e = tm.after()))
       return hip_status(e);
@@ -351,6 +367,36 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
     gg.tile_n = plan.tile;
     if (plan.split) gg.g.N = c->hc_mult * c->hidden;   // key channels only
     if ((e = tm.before()) || (e = launch_gemm_gate_bf16(gg, s)) || (e = tm.after())) return hip_status(e);
+    if (tail) {
+      DecodeTailArgs dt;
+      dt.partials = w.part;
+      dt.v = w.v;
+      dt.conv_w = p->conv_w;
+      dt.out = out;
+      dt.past = w.past;
+      dt.ids = ids;
+      dt.remap = p->remap;
+      dt.vocab = c->vocab;
+      dt.pad_id = c->pad_id;
+      dt.tok_ring = st->tok_ring;
+      dt.v_ring = st->v_ring;
+      dt.g_ring = st->g_ring;
+      dt.n_past = st->n_past;
+      dt.batch = c->batch;
+      dt.hc = c->hc_mult;
+      dt.d = c->hidden;
+      dt.ksize = c->conv_kernel;
+      dt.dil = c->conv_dilation;
+      dt.n_part = c->hidden / 128;
+      dt.ring_len = ring_len(c);
+      dt.tok_ring_len = max_order(c) - 1;
+      dt.eps = c->norm_eps;
+      dt.clamp = c->gate_clamp;
+      dt.inv_sqrt_d = (float)(1.0 / sqrt((double)c->hidden));
+      dt.bf16 = bf16;
+      if ((e = tm.before()) || (e = launch_decode_tail(dt, s)) || (e = tm.after())) return hip_status(e);
+      return ENGRAM_OK;
+    }
     if (plan.split) {   // value channels: V = W_v e into the workspace
       GemmArgs gv = gemm_args(c, p, e_rows, w.v);
       gv.B = (const uint8_t*)p->w_kv + (int64_t)c->hc_mult * c->hidden * emb_dim(c) * esize(c);
@@ -773,12 +819,13 @@ engram_status engram_gather_host(const engram_config* cfg, const void* tables, c
   return ENGRAM_OK;
 }
 
-const char* engram_forward_kernel_name(const engram_config* cfg, int32_t i) {
+const char* engram_forward_kernel_name(const engram_config* cfg, int32_t with_state, int32_t i) {
   if (validate(cfg) || i < 0) return nullptr;
+  if (decode_tail_path(cfg, with_state != 0, false)) return i < 3 ? kDecodeKernels[i] : nullptr;
   const GatePlan plan = gate_plan(cfg);
-  if (plan.split) return i < 6 ? kSplitKernels[i] : nullptr;
-  if (i >= 5) return nullptr;
-  return plan.tile ? kFusedKernels[i] : kForwardKernels[i];
+  const char* const* names = plan.split ? kSplitKernels : plan.tile ? kFusedKernels : kForwardKernels;
+  const int n = (plan.split ? 6 : 5) - (with_state ? 0 : 1);   // advance_state is last
+  return i < n ? names[i] : nullptr;
 }
 
 const char* engram_status_string(engram_status s) {

@@ -23,6 +23,37 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool bf16) {
   return bf16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
+// The gate from the fused projection's partial sums of one (token, branch),
+// computed by an aligned group of 8 lanes (lane l = lane % 8 adds partials l,
+// l+8, ...; xor shuffles combine the 8 sums; every lane of the group returns
+// g): rk = (sum K^2 / d + eps)^-1/2, rq alike, s = (sum K gk gq Q) rk rq / sqrt(d),
+// g = sigmoid(sign(s) sqrt(max(|s|, clamp))).  All 8 lanes must call it.
+__device__ __forceinline__ float gate_from_partials8(const float4* p, int n_part, bool ok, int d, float eps,
+                                                     float clamp, float inv_sqrt_d) {
+  const int l = threadIdx.x & 7;
+  float kk = 0.f, qq = 0.f, kq = 0.f;
+  if (ok)
+    for (int t = l; t < n_part; t += 8) {
+      const float4 v = p[t];
+      kk += v.x;
+      qq += v.y;
+      kq += v.z;
+    }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    kk += __shfl_xor(kk, o, 64);
+    qq += __shfl_xor(qq, o, 64);
+    kq += __shfl_xor(kq, o, 64);
+  }
+  const float inv_d = 1.f / (float)d;
+  const float rk = 1.f / sqrtf(kk * inv_d + eps);
+  const float rq = 1.f / sqrtf(qq * inv_d + eps);
+  const float s = kq * rk * rq * inv_sqrt_d;
+  const float sgn = s > 0.f ? 1.f : (s < 0.f ? -1.f : 0.f);
+  const float act = sgn * sqrtf(fmaxf(fabsf(s), clamp));
+  return 1.f / (1.f + expf(-act));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -55,6 +86,7 @@ struct GatherArgs {
   uint8_t* e_out;           // [N][E] or null
   const int32_t* tok_ring;  // [B][max_order-1] or null
   const int64_t* n_past;    // [B] or null
+  int64_t* past_out;        // [B] or null: n_past of each sequence before this call
   int32_t batch, seqlen;
   int32_t row_bytes;        // head_dim * element size
 };
@@ -224,5 +256,27 @@ struct AdvanceArgs {
 };
 
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
+
+// One decode step (T = 1) with a state after the fused projection: the gates
+// from the partial sums, the conv over the rings' history and the state
+// update, in one kernel (replaces gate_finalize, short_conv and advance_state).
+struct DecodeTailArgs {
+  const float4* partials;  // [B][hc][n_part]
+  const void* v;           // [B][d] this step's value rows
+  const void* conv_w;      // [hc][d][K]
+  void* out;               // [B][hc][d]
+  const int64_t* past;     // [B] n_past before the step (from the hash kernel)
+  const int32_t* ids;      // [B] raw ids of the step
+  const int32_t* remap;    // or null
+  int32_t vocab, pad_id;
+  int32_t* tok_ring;       // [B][tok_ring_len]
+  void* v_ring;            // [B][ring_len][d]
+  float* g_ring;           // [B][ring_len][hc]
+  int64_t* n_past;         // [B]
+  int32_t batch, hc, d, ksize, dil, n_part, ring_len, tok_ring_len;
+  float eps, clamp, inv_sqrt_d;
+  bool bf16;
+};
+hipError_t launch_decode_tail(const DecodeTailArgs& a, hipStream_t s);
 
 }  // namespace engram

@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int n_it = min(kConvIters, (T - t_first + D - 1) / D);   // positions this thread visits
 
   const int64_t d = a.d;
-  const int R = (KS - 1) * D;
+  const int R = (KS - 1) * D + 1;   // ring length of the state (history plus the slot a decode step fills)
   const int64_t past = a.n_past ? a.n_past[b] : 0;
 
   // every V slice and gate of the walk is loaded before any is used, so a
@@ -301,6 +301,108 @@ __global__ void __launch_bounds__(256) k_advance(AdvanceArgs a) {
   if (threadIdx.x == 0) a.n_past[b] = past + T;
 }
 
+// One decode step (T = 1) with a state, after the fused projection.  Block
+// (channel block cb, sequence b): threads over (branch, 8 channels) as in
+// k_conv.  The gates of the branches the block spans come from the partial
+// sums (8 lanes each, as gate_finalize); the output is the conv over the
+// rings' history with k_conv's arithmetic; then the new position enters the
+// rings at slot past % R.  The rings hold R = (K-1) D + 1 positions, so that
+// slot is never one the history reads (those are past - m D, 0 < m D < R),
+// and the block may write it while other blocks still read the history.
+// Every block reads n_past from the hash kernel's snapshot; one thread then
+// advances n_past and the token ring.
+template <bool BF16, int KS>
+__global__ void __launch_bounds__(256) k_decode_tail(DecodeTailArgs a) {
+  __shared__ float sg[ENGRAM_MAX_BRANCHES];
+  const int cb = blockIdx.x, b = blockIdx.y;
+  const int groups = a.d >> 3;
+  const int gx = cb * 256 + threadIdx.x;
+  const bool active = gx < a.hc * groups;
+  const int h = active ? gx / groups : 0;
+  const int c0 = (gx - h * groups) * 8;
+  const int h_lo = cb * 256 / groups;
+  const int nb = min(a.hc - 1, (cb * 256 + 255) / groups) - h_lo + 1;
+  const int64_t past = a.past[b];
+  const int64_t d = a.d, R = a.ring_len;
+  const int64_t new_slot = (int64_t)b * R + past % R;
+
+  if (threadIdx.x < 8 * nb) {   // whole 8-lane groups
+    const int hb = threadIdx.x >> 3, hh = h_lo + hb;
+    const float g = gate_from_partials8(a.partials + ((int64_t)b * a.hc + hh) * a.n_part, a.n_part, true, a.d,
+                                        a.eps, a.clamp, a.inv_sqrt_d);
+    if ((threadIdx.x & 7) == 0) {
+      sg[hb] = g;
+      if (cb == hh * groups / 256) a.g_ring[new_slot * a.hc + hh] = g;   // the block with the branch's first channels
+    }
+  }
+  __syncthreads();
+  if (active) {
+    const float g = sg[h - h_lo];
+    float w[KS][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
+    u32x4 lo, hi = u32x4{0, 0, 0, 0};
+    load_raw8<BF16>(a.v, (int64_t)b * d + c0, lo, hi);
+    float cur[8];
+    unpack8<BF16>(lo, hi, g, cur);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = fmaf(w[KS - 1][i], cur[i], cur[i]);
+#pragma unroll
+    for (int j = 0; j < KS - 1; j++) {
+      const int64_t p = past - (int64_t)(KS - 1 - j) * a.dil;   // history position of tap j
+      float hv[8];
+      if (p < 0) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) hv[i] = 0.f;
+      } else {
+        const int64_t slot = (int64_t)b * R + p % R;
+        u32x4 l, u = u32x4{0, 0, 0, 0};
+        load_raw8<BF16>(a.v_ring, slot * d + c0, l, u);
+        unpack8<BF16>(l, u, a.g_ring[slot * a.hc + h], hv);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = fmaf(w[j][i], hv[i], acc[i]);
+    }
+    store8(a.out, ((int64_t)b * a.hc + h) * d + c0, BF16, acc);
+    if (h == 0) {   // the value row enters the ring (branch 0's threads cover every channel once)
+      if constexpr (BF16) {
+        *(u32x4*)((uint16_t*)a.v_ring + new_slot * d + c0) = lo;
+      } else {
+        *(u32x4*)((float*)a.v_ring + new_slot * d + c0) = lo;
+        *(u32x4*)((float*)a.v_ring + new_slot * d + c0 + 4) = hi;
+      }
+    }
+  }
+  if (cb == 0 && threadIdx.x == 0) {
+    if (a.tok_ring_len > 0) {
+      const int32_t id = a.ids[b];
+      int32_t x = a.pad_id;
+      if (id >= 0 && id < a.vocab) x = a.remap ? a.remap[id] : id;
+      a.tok_ring[(int64_t)b * a.tok_ring_len + past % a.tok_ring_len] = x;
+    }
+    a.n_past[b] = past + 1;
+  }
+}
+
+template <bool BF16>
+hipError_t decode_tail_dispatch(const DecodeTailArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.ksize) {
+    case 1: k_decode_tail<BF16, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_decode_tail<BF16, 2><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_decode_tail<BF16, 3><<<grid, 256, 0, s>>>(a); break;
+    case 4: k_decode_tail<BF16, 4><<<grid, 256, 0, s>>>(a); break;
+    case 5: k_decode_tail<BF16, 5><<<grid, 256, 0, s>>>(a); break;
+    case 6: k_decode_tail<BF16, 6><<<grid, 256, 0, s>>>(a); break;
+    case 7: k_decode_tail<BF16, 7><<<grid, 256, 0, s>>>(a); break;
+    case 8: k_decode_tail<BF16, 8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <bool BF16, int IT>
 hipError_t conv_dispatch(const ConvArgs& a, dim3 grid, hipStream_t s) {
   switch (a.ksize) {
@@ -339,6 +441,13 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil * ((lanes + 255) / 256)));
   if (it == 16) return a.bf16 ? conv_dispatch<true, 16>(a, grid, s) : conv_dispatch<false, 16>(a, grid, s);
   return a.bf16 ? conv_dispatch<true, 8>(a, grid, s) : conv_dispatch<false, 8>(a, grid, s);
+}
+
+hipError_t launch_decode_tail(const DecodeTailArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  if (a.ring_len < 1) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.hc * (a.d / 8) + 255) / 256), (unsigned)a.batch);
+  return a.bf16 ? decode_tail_dispatch<true>(a, grid, s) : decode_tail_dispatch<false>(a, grid, s);
 }
 
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {

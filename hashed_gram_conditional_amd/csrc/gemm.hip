@@ -563,36 +563,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   }
 }
 
-// g from the fused GEMM's partial sums: 8 lanes per (token, branch), lane l
-// adding partials l, l+8, ... (consecutive lanes read consecutive 16-byte
-// partials), then the 8 lane sums combined by xor shuffles in a fixed order.
+// g from the fused GEMM's partial sums: 8 lanes per (token, branch)
+// (gate_from_partials8), consecutive lanes on consecutive 16-byte partials.
 __global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
-  const int l = threadIdx.x & 7;
   const bool ok = i < (int64_t)a.n_tok * a.hc;
-  const float4* p = a.partials + (ok ? i : 0) * a.n_part;
-  float kk = 0.f, qq = 0.f, kq = 0.f;
-  if (ok)
-    for (int t = l; t < a.n_part; t += 8) {
-      const float4 v = p[t];
-      kk += v.x;
-      qq += v.y;
-      kq += v.z;
-    }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) {
-    kk += __shfl_xor(kk, o, 64);
-    qq += __shfl_xor(qq, o, 64);
-    kq += __shfl_xor(kq, o, 64);
-  }
-  if (!ok || l != 0) return;
-  const float inv_d = 1.f / (float)a.d;
-  const float rk = 1.f / sqrtf(kk * inv_d + a.eps);
-  const float rq = 1.f / sqrtf(qq * inv_d + a.eps);
-  const float s = kq * rk * rq * a.inv_sqrt_d;
-  const float sgn = s > 0.f ? 1.f : (s < 0.f ? -1.f : 0.f);
-  const float act = sgn * sqrtf(fmaxf(fabsf(s), a.clamp));
-  a.g_out[i] = 1.f / (1.f + expf(-act));
+  const float g = gate_from_partials8(a.partials + (ok ? i : 0) * a.n_part, a.n_part, ok, a.d, a.eps, a.clamp,
+                                      a.inv_sqrt_d);
+  if (ok && (threadIdx.x & 7) == 0) a.g_out[i] = g;
 }
 
 // float32 path: a plain LDS-tiled FMA GEMM, 64x64 tile, 4x4 outputs per thread.

@@ -103,6 +103,11 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
     const int ntok = (int)min((int64_t)kTokens, N - n0);
 
     if (compute_hash) {
+      if (a.past_out)   // n_past before this call, for kernels that advance the state later
+        for (int ti = tid; ti < ntok; ti += kThreads) {
+          const int64_t n = n0 + ti, b = n / a.seqlen;
+          if (n - b * a.seqlen == 0) a.past_out[b] = a.n_past ? a.n_past[b] : 0;
+        }
       stage_window(hc, a, s_x, n0, ntok);
       for (int pr = tid; pr < ntok * H; pr += kThreads) {
         const int ti = pr / H, h = pr - ti * H;

@@ -103,8 +103,8 @@ typedef struct engram_params {
  * sequence, whose rings need no initialisation. */
 typedef struct engram_state {
   int32_t *tok_ring;        /* [B][max_order-1] compressed ids (unused when max_order == 1) */
-  void *v_ring;             /* [B][(conv_kernel-1)*conv_dilation][hidden] dtype, value projections */
-  float *g_ring;            /* [B][(conv_kernel-1)*conv_dilation][hc_mult] gates */
+  void *v_ring;             /* [B][R][hidden] dtype, value projections; R = (conv_kernel-1)*conv_dilation + 1 */
+  float *g_ring;            /* [B][R][hc_mult] gates */
   int64_t *n_past;          /* [B] */
 } engram_state;
 
@@ -248,8 +248,9 @@ engram_status engram_forward_timed(const engram_config *cfg, const engram_params
                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
                                    int32_t n_events, int32_t *n_kernels);
 
-/* Static name of the i-th kernel engram_forward launches for cfg (NULL past the end). */
-const char *engram_forward_kernel_name(const engram_config *cfg, int32_t i);
+/* Static name of the i-th kernel engram_forward launches for cfg, with or
+ * without a state (NULL past the end). */
+const char *engram_forward_kernel_name(const engram_config *cfg, int32_t with_state, int32_t i);
 
 /* Static description of a status code. */
 const char *engram_status_string(engram_status status);

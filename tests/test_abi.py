@@ -59,7 +59,7 @@ def test_workspace_and_state_sizes(eg):
     ws = eg.workspace_size(c)
     assert ws >= N * E * 2 + N * (hc + 1) * d * 2 + N * hc * 4
     assert ws % 256 == 0
-    R = 3 * 3
+    R = 3 * 3 + 1
     assert eg.state_bytes_per_sequence(c) == 2 * 4 + R * d * 2 + R * hc * 4 + 8
 
 

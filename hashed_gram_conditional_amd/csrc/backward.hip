@@ -91,13 +91,50 @@ __device__ __forceinline__ void st4(void* p, int64_t i, bool bf16, const float* 
 
 constexpr int kConvCh = 4;   // channels per thread of the conv backward
 
+// v + v of another lane by a DPP move (no LDS): CTRL 0xB1 / 0x4E are the quad
+// permutations of lane l ^ 1 / l ^ 2; 0x124 / 0x128 rotate a 16-lane row by 4 / 8
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the lanes that share lane bits >= log2(hc) (the hc lanes of one
+// channel group), hc a power of two up to 16.
+__device__ __forceinline__ float sum_over_branches(float v, int hc) {
+  if (hc > 1) v = add_dpp<0xB1>(v);
+  if (hc > 2) v = add_dpp<0x4E>(v);
+  for (int o = 4; o < hc; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the lanes with the same lane % hc (one branch, every channel group
+// of the wave); the lanes with lane < hc hold it.  Rotations by multiples of
+// hc within a row keep lane % hc, so they sum a branch's lanes of the row.
+__device__ __forceinline__ float sum_over_channels(float v, int hc) {
+  if (hc == 1) v = add_dpp<0xB1>(v);
+  if (hc <= 2) v = add_dpp<0x4E>(v);
+  if (hc <= 4) v = add_dpp<0x124>(v);
+  if (hc <= 8) v = add_dpp<0x128>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // Block: 64 lanes over (branch, 4 channels) x 4 spans of `span` consecutive
 // positions of one sequence.  A thread walks its span one residue r mod D at a
 // time in steps of D, so the dy values ahead (dy[t + m D], m < K) and the
 // gated values behind (Vg[t - m D]) are rings in registers: one new load of
 // each per step.  The tap sums of the 4 spans are added in LDS in span order
 // and stored as the block's partial row.
-template <bool BF16, int KS>
+//
+// FUSE (hc a power of two): lanes are ordered branch-minor (lane = channel
+// group * hc + branch), so the dVg of a step never reaches memory: the hc
+// lanes of a channel group add g dVg into dV (xor shuffles over the low lane
+// bits) and the lanes of one branch add dVg . V over the wave's 64 channels
+// into one partial of dg (shuffles over the high bits), both in a fixed order.
+// Otherwise (lane = branch * groups + channel group) dVg is stored for the
+// gate kernel.
+template <bool BF16, int KS, bool FUSE>
 __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
   constexpr int CH = kConvCh;
   __shared__ float red[3][KS * CH][64];
@@ -105,8 +142,14 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
   const int groups = a.d / CH;
   const int gx = blockIdx.x * 64 + lane;
   const bool active = gx < a.hc * groups;
-  const int h = active ? gx / groups : 0;
-  const int c0 = active ? (gx - h * groups) * CH : 0;
+  int h, c0;
+  if (FUSE) {
+    h = gx % a.hc;
+    c0 = active ? gx / a.hc * CH : 0;
+  } else {
+    h = active ? gx / groups : 0;
+    c0 = active ? (gx - h * groups) * CH : 0;
+  }
   const int T = a.seqlen, D = a.dil;
   const int blocks_per_seq = (T + 4 * a.span - 1) / (4 * a.span);
   const int b = blockIdx.y / blocks_per_seq;
@@ -121,22 +164,23 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; i++) dw[j][i] = 0.f;
 
-  if (active) {
+  // FUSE: every lane walks (inactive ones on zeros) so the shuffles see all 64
+  if (FUSE || active) {
     float w[KS][CH];
 #pragma unroll
     for (int i = 0; i < CH; i++)
 #pragma unroll
-      for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
+      for (int j = 0; j < KS; j++) w[j][i] = active ? ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16) : 0.f;
     const int64_t dy_col = (int64_t)h * d + c0, v_col = hcd + c0;
-    // 0 outside [0, T)
-    auto load_dy = [&](int t, float* v) { ld4_or0(a.dy, (row0 + (t < T ? t : 0)) * hcd + dy_col, t < T, BF16, v); };
-    auto load_vg = [&](int t, float* v) {
-      const bool ok = t >= 0 && t < T;
+    // 0 outside [0, T) (and for inactive lanes)
+    auto load_dy = [&](int t, float* v) {
+      ld4_or0(a.dy, (row0 + (t < T ? t : 0)) * hcd + dy_col, active && t < T, BF16, v);
+    };
+    auto load_v = [&](int t, float* v, float& g) {   // V at t and the gate of this branch
+      const bool ok = active && t >= 0 && t < T;
       const int64_t n = row0 + (ok ? t : 0);
       ld4_or0(a.kv, n * O + v_col, ok, BF16, v);
-      const float g = ok ? a.stats[n * a.hc + h].x : 0.f;
-#pragma unroll
-      for (int i = 0; i < CH; i++) v[i] *= g;
+      g = ok ? a.stats[n * a.hc + h].x : 0.f;
     };
     for (int r = 0; r < D; r++) {
       const int t0 = t_lo + r;
@@ -146,10 +190,18 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
       // (s - m) mod KS holds g V at t - m D (m < KS), t = t0 + s D; the loop
       // is unrolled over the ring, so every slot index is a constant
       float F[KS][CH], P[KS][CH];
+      // FUSE: results kept for a batched store (see below); n < 0: none held
+      float keep_dv[CH] = {0.f, 0.f, 0.f, 0.f}, keep_g = 0.f;
+      int64_t keep_dv_n = -1, keep_g_n = -1;
 #pragma unroll
       for (int m = 0; m + 1 < KS; m++) load_dy(t0 + m * D, F[m]);
 #pragma unroll
-      for (int m = 1; m < KS; m++) load_vg(t0 - m * D, P[KS - m]);
+      for (int m = 1; m < KS; m++) {
+        float g;
+        load_v(t0 - m * D, P[KS - m], g);
+#pragma unroll
+        for (int i = 0; i < CH; i++) P[KS - m][i] *= g;
+      }
       for (int s0 = 0; s0 < n_steps; s0 += KS) {
 #pragma unroll
         for (int u = 0; u < KS; u++) {
@@ -157,7 +209,10 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
           if (st >= n_steps) break;
           const int t = t0 + st * D;
           load_dy(t + (KS - 1) * D, F[(u + KS - 1) % KS]);   // the step's new dy (m = KS-1)
-          load_vg(t, P[u]);                                  // and g V (m = 0)
+          float V[CH], g;                                    // and V, g at t (m = 0)
+          load_v(t, V, g);
+#pragma unroll
+          for (int i = 0; i < CH; i++) P[u][i] = V[i] * g;
           float acc[CH];
 #pragma unroll
           for (int i = 0; i < CH; i++) acc[i] = F[u][i];
@@ -168,7 +223,45 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
               acc[i] = fmaf(w[j][i], F[(u + KS - 1 - j) % KS][i], acc[i]);
               dw[j][i] = fmaf(F[u][i], P[(u + 1 + j) % KS][i], dw[j][i]);
             }
-          st4(a.dvg, (row0 + t) * hcd + dy_col, BF16, acc);
+          if constexpr (FUSE) {
+            float dv[CH], pg = 0.f;
+#pragma unroll
+            for (int i = 0; i < CH; i++) {
+              dv[i] = g * acc[i];
+              pg = fmaf(acc[i], V[i], pg);
+            }
+#pragma unroll
+            for (int i = 0; i < CH; i++) dv[i] = sum_over_branches(dv[i], a.hc);
+            pg = sum_over_channels(pg, a.hc);
+            // Stores are batched: a store instruction costs about the same for
+            // a few lanes as for the whole wave.  All hc lanes of a channel
+            // group hold the same dV (a butterfly), so lane h keeps the dV of
+            // steps st = h mod hc and the wave stores every hc steps; lane
+            // u hc + h keeps branch h's dg partial of step u of each run of
+            // 64/hc steps, stored once per run.
+            const int64_t n = row0 + t;
+            const int G = 64 / a.hc;
+            if (st % a.hc == h) {
+#pragma unroll
+              for (int i = 0; i < CH; i++) keep_dv[i] = dv[i];
+              keep_dv_n = n;
+            }
+            if (st % G == lane / a.hc) {
+              keep_g = pg;
+              keep_g_n = n;
+            }
+            const bool last = st + 1 == n_steps;
+            if (st % a.hc == a.hc - 1 || last) {
+              if (active && keep_dv_n >= 0) st4(a.dkv, keep_dv_n * O + hcd + c0, BF16, keep_dv);
+              keep_dv_n = -1;
+            }
+            if (st % G == G - 1 || last) {
+              if (keep_g_n >= 0) a.dgp[(keep_g_n * a.n_dgp + blockIdx.x) * a.hc + h] = keep_g;
+              keep_g_n = -1;
+            }
+          } else {
+            st4(a.dvg, (row0 + t) * hcd + dy_col, BF16, acc);
+          }
         }
       }
     }
@@ -192,8 +285,9 @@ __global__ void __launch_bounds__(256) k_conv_bwd(ConvBwdArgs a) {
 }
 
 // Block: tpb consecutive tokens, all branches.
-// Phase 1 (one wave per token): dg of every branch (V read once), dV into the
-// value block of dkv, and per (token, branch) coef, ak = ds s rk^2 / d,
+// Phase 1 (one wave per token): dg of every branch (V read once) and dV into
+// the value block of dkv -- or, after the fused conv kernel, dg from its
+// per-64-channel partials -- and per (token, branch) coef, ak = ds s rk^2 / d,
 // bq = ds s rq^2 / d into LDS.  Phase 2 (a thread per 8 channels of one
 // branch, looping over the block's tokens): dK, dQ and the partial S.
 template <bool BF16, int HB>   // HB >= hc: bound of the per-branch arrays of phase 1
@@ -214,6 +308,12 @@ __global__ void __launch_bounds__(256) k_gate_bwd(GateBwdArgs a) {
       g[h] = h < hc ? a.stats[n * hc + h].x : 0.f;
       dgp[h] = 0.f;
     }
+    if (a.dgp) {   // dg partials per 64 channels from the conv kernel (dV is already stored)
+#pragma unroll
+      for (int h = 0; h < HB; h++)
+        if (h < hc)
+          for (int k = lane; k < a.n_dgp; k += 64) dgp[h] += a.dgp[(n * a.n_dgp + k) * hc + h];
+    } else {
 #pragma unroll 2
     for (int64_t c = lane * 8; c < d; c += 512) {
       float V[8], dV[8];
@@ -233,6 +333,7 @@ __global__ void __launch_bounds__(256) k_gate_bwd(GateBwdArgs a) {
         }
       }
       st8(a.dkv, n * O + hcd + c, BF16, dV);
+    }
     }
 #pragma unroll
     for (int h = 0; h < HB; h++) {
@@ -391,17 +492,17 @@ __global__ void __launch_bounds__(256) k_scatter_add(HashConsts hc, const int32_
   atomicAdd(&d_tables[row * Dh + j], de[i]);
 }
 
-template <bool BF16>
+template <bool BF16, bool FUSE>
 hipError_t conv_bwd_dispatch(const ConvBwdArgs& a, dim3 grid, hipStream_t s) {
   switch (a.ksize) {
-    case 1: k_conv_bwd<BF16, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_conv_bwd<BF16, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_conv_bwd<BF16, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: k_conv_bwd<BF16, 4><<<grid, 256, 0, s>>>(a); break;
-    case 5: k_conv_bwd<BF16, 5><<<grid, 256, 0, s>>>(a); break;
-    case 6: k_conv_bwd<BF16, 6><<<grid, 256, 0, s>>>(a); break;
-    case 7: k_conv_bwd<BF16, 7><<<grid, 256, 0, s>>>(a); break;
-    case 8: k_conv_bwd<BF16, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_conv_bwd<BF16, 1, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_conv_bwd<BF16, 2, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_conv_bwd<BF16, 3, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 4: k_conv_bwd<BF16, 4, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 5: k_conv_bwd<BF16, 5, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 6: k_conv_bwd<BF16, 6, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 7: k_conv_bwd<BF16, 7, FUSE><<<grid, 256, 0, s>>>(a); break;
+    case 8: k_conv_bwd<BF16, 8, FUSE><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -416,11 +517,19 @@ int64_t conv_bwd_rows(int32_t batch, int32_t seqlen) {
   return (int64_t)batch * ((seqlen + 4 * span - 1) / (4 * span));
 }
 
+bool conv_bwd_fused(int32_t hc) { return hc >= 1 && hc <= 16 && (hc & (hc - 1)) == 0; }
+
+int conv_bwd_dg_parts(int32_t hc, int32_t d) { return (hc * (d / kConvCh) + 63) / 64; }
+
 hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s) {
   if ((int64_t)a.batch * a.seqlen == 0) return hipSuccess;
   const int lanes = a.hc * (a.d / kConvCh);
   dim3 grid((unsigned)((lanes + 63) / 64), (unsigned)conv_bwd_rows(a.batch, a.seqlen));
-  return a.bf16 ? conv_bwd_dispatch<true>(a, grid, s) : conv_bwd_dispatch<false>(a, grid, s);
+  if (a.dgp != nullptr) {
+    if (!conv_bwd_fused(a.hc) || a.n_dgp != (int)grid.x) return hipErrorInvalidValue;
+    return a.bf16 ? conv_bwd_dispatch<true, true>(a, grid, s) : conv_bwd_dispatch<false, true>(a, grid, s);
+  }
+  return a.bf16 ? conv_bwd_dispatch<true, false>(a, grid, s) : conv_bwd_dispatch<false, false>(a, grid, s);
 }
 
 int gate_bwd_tpb(int64_t n_tok) {

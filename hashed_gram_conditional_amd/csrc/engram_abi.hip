@@ -171,7 +171,8 @@ struct BwdWorkspace {
   void* kv;         // [N][hc+1][d]
   float4* stats;    // [N][hc] (g, s, rk, rq)
   float* g;         // [N][hc] gates (the conv of engram_forward_train reads them)
-  void* dvg;        // [N][hc][d] dtype: gradient of the gated values
+  void* dvg;        // [N][hc][d] dtype: gradient of the gated values (hc not a power of two)
+  float* dgp;       // [N][n_dgp][hc]: dg partials of the fused conv kernel (hc a power of two)
   void* dkv;        // [N][hc+1][d]
   float* de;        // [N][E]
   void* wT;         // [E][(hc+1)d]
@@ -204,7 +205,10 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.kv = take((size_t)(N * O * es));
   w.stats = (float4*)take((size_t)N * c->hc_mult * sizeof(float4));
   w.g = (float*)take((size_t)N * c->hc_mult * sizeof(float));
-  w.dvg = take((size_t)(N * c->hc_mult * c->hidden * es));
+  if (conv_bwd_fused(c->hc_mult))
+    w.dgp = (float*)take((size_t)N * c->hc_mult * conv_bwd_dg_parts(c->hc_mult, c->hidden) * sizeof(float));
+  else
+    w.dvg = take((size_t)(N * c->hc_mult * c->hidden * es));
   w.dkv = take((size_t)(N * O * es));
   w.de = (float*)take((size_t)(N * E) * sizeof(float));
   w.wT = take((size_t)(E * O * es));
@@ -515,6 +519,11 @@ engram_status gradients(const engram_config* cfg, const engram_params* prm, cons
   cb.dvg = w.dvg;
   cb.part = w.cpart;
   cb.span = conv_bwd_span(N);
+  if (w.dgp) {
+    cb.dkv = w.dkv;
+    cb.dgp = w.dgp;
+    cb.n_dgp = conv_bwd_dg_parts(cfg->hc_mult, cfg->hidden);
+  }
   cb.batch = cfg->batch;
   cb.seqlen = cfg->seqlen;
   cb.hc = cfg->hc_mult;
@@ -525,6 +534,8 @@ engram_status gradients(const engram_config* cfg, const engram_params* prm, cons
   if ((e = launch_conv_bwd(cb, stream))) return hip_status(e);
   GateBwdArgs gb;
   gb.dvg = w.dvg;
+  gb.dgp = w.dgp;
+  gb.n_dgp = cb.n_dgp;
   gb.kv = w.kv;
   gb.hidden = hidden;
   gb.gamma_k = prm->gamma_k;

@@ -194,21 +194,30 @@ struct ConvBwdArgs {
   const void* kv;          // [N][hc+1][d] (values in the last block)
   const float4* stats;     // [N][hc] (g, s, rk, rq)
   const void* conv_w;      // [hc][d][K]
-  void* dvg;               // [N][hc][d] dtype
+  void* dvg;               // [N][hc][d] dtype (unfused)
   float* part;             // [conv_bwd_rows][hc][d][K]: tap sums of each block's positions
+  // fused (conv_bwd_fused(hc)): dV into the value block of dkv [N][hc+1][d] and
+  // dg partials [N][n_dgp][hc] (one per 64 channels of the lane order) instead of dvg
+  void* dkv = nullptr;
+  float* dgp = nullptr;
+  int32_t n_dgp = 0;
   int32_t batch, seqlen, hc, d, ksize, dil;
   int32_t span;            // positions per thread (a block covers 4 spans of one sequence)
   bool bf16;
 };
 // positions per thread of the conv backward, and the partial rows it writes
 int conv_bwd_span(int64_t n_tok);
+bool conv_bwd_fused(int32_t hc);              // hc a power of two up to 16
+int conv_bwd_dg_parts(int32_t hc, int32_t d);  // dg partials per (token, branch) of the fused kernel
 int64_t conv_bwd_rows(int32_t batch, int32_t seqlen);
 hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
 
 // gate and RMSNorm gradients (dK, d hidden) and dV; the gammas' gradients as
 // per-block partial sums S = sum_n coef K Q (d gamma_k = gamma_q S, d gamma_q = gamma_k S)
 struct GateBwdArgs {
-  const void* dvg;         // [N][hc][d] dtype
+  const void* dvg;         // [N][hc][d] dtype, or null with dgp
+  const float* dgp = nullptr;   // [N][n_dgp][hc] dg partials (fused conv kernel; dV already in dkv)
+  int32_t n_dgp = 0;
   const void* kv;          // [N][hc+1][d]
   const void* hidden;      // [N][hc][d]
   const void* gamma_k;     // [hc][d]

@@ -16,12 +16,17 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC
                "-I" + os.path.join(ROOT, "include")]
 
 
+# the sources the forward kernels are built from (the gradients' kernels are not among them)
+FORWARD_SOURCES = [f for f in SOURCES if f != "backward.hip"]
+
+
 def source_hash() -> str:
-    """sha256 over the library's sources and headers (identifies a kernel build)."""
+    """sha256 over the forward kernels' sources and headers: identifies the
+    build that measured HBM traffic per forward kernel describes."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(SOURCES + HEADERS):
+    for f in sorted(FORWARD_SOURCES + HEADERS):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

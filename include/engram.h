@@ -242,7 +242,7 @@ engram_status engram_backward_saved(const engram_config *cfg, const engram_param
 /* Same as engram_forward, additionally recording events[2i] / events[2i+1]
  * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,
  * for i < n_events/2.  Returns the number of kernels in *n_kernels (nullable).
- * Names of those kernels: engram_forward_kernel_name(cfg, i). */
+ * Names of those kernels: engram_forward_kernel_name(cfg, st != NULL, i). */
 engram_status engram_forward_timed(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
                                    const void *hidden, engram_state *st, void *out, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,

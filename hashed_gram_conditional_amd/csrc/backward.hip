@@ -44,10 +44,10 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, bool bf16, float* 
 __device__ __forceinline__ void st8(void* p, int64_t i, bool bf16, const float* v) {
   if (bf16) {
     uint4 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
     *(uint4*)((uint16_t*)p + i) = u;
   } else {
     *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
@@ -81,8 +81,8 @@ __device__ __forceinline__ void ld4_or0(const void* p, int64_t i, bool ok, bool 
 __device__ __forceinline__ void st4(void* p, int64_t i, bool bf16, const float* v) {
   if (bf16) {
     uint2 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
     *(uint2*)((uint16_t*)p + i) = u;
   } else {
     *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);

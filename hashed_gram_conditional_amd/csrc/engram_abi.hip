@@ -54,7 +54,7 @@ engram_status check_params(const engram_config* c, const engram_params* p) {
       p->gamma_q == nullptr || p->conv_w == nullptr)
     return ENGRAM_EINVAL;
   if (!aligned(p->tables, 16) || !aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) ||
-      !aligned(p->conv_w, 4))
+      !aligned(p->conv_w, 16))
     return ENGRAM_EINVAL;
   return ENGRAM_OK;
 }
@@ -78,7 +78,7 @@ engram_status check_params_no_tables(const engram_config* c, const engram_params
   (void)c;
   if (p == nullptr || p->w_kv == nullptr || p->gamma_k == nullptr || p->gamma_q == nullptr || p->conv_w == nullptr)
     return ENGRAM_EINVAL;
-  if (!aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) || !aligned(p->conv_w, 4))
+  if (!aligned(p->w_kv, 16) || !aligned(p->gamma_k, 16) || !aligned(p->gamma_q, 16) || !aligned(p->conv_w, 16))
     return ENGRAM_EINVAL;
   return ENGRAM_OK;
 }

@@ -12,11 +12,18 @@ namespace engram {
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// round to nearest even; NaN stays NaN (quiet)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// Round to nearest even; NaN stays NaN (quiet).  gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction); on all 2^32 float patterns
+// its result equals the integer rounding (u + 0x7FFF + bit 16 of u) >> 16, with
+// NaNs quieted by setting bit 6 of the result.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// lo in bits 0-15, hi in bits 16-31
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool bf16) {

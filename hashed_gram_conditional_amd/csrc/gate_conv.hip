@@ -14,12 +14,12 @@
 // walk-through, yaoyuxiang.cn/news/830577, section 2.2-3: depthwise causal
 // conv, kernel 4, dilation = largest order):
 //   y_h[t] = Vg_h[t] + sum_j w_h[j] Vg_h[t - (K-1-j) D],  Vg_h = g_h V
-// A thread owns 8 channels of one branch and walks the positions
-// t0+r, t0+r+D, t0+r+2D, ... of one residue r mod D: every conv tap of the
-// next position is a position it has already visited, so the K-1 taps of
-// history stay in registers and each step loads one 16-byte slice of V, one
-// gate and writes one 16-byte slice of y.  The taps (8 channels x K) also stay
-// in registers for the whole walk.
+// A wavefront walks the positions t0+r, t0+r+D, t0+r+2D, ... of one residue
+// r mod D over 256 channels, for every branch: every conv tap of the next
+// position is a position already visited, so the history stays in registers,
+// and each value slice is loaded once for all branches.
+#include <type_traits>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -50,10 +50,10 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, bool bf16, float
 __device__ __forceinline__ void store8(void* p, int64_t i, bool bf16, const float* v) {
   typedef uint32_t w4 __attribute__((ext_vector_type(4)));
   if (bf16) {
-    const w4 u = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                  (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16),
-                  (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16),
-                  (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16)};
+    const w4 u = {pack_bf16x2(v[0], v[1]),
+                  pack_bf16x2(v[2], v[3]),
+                  pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7])};
     __builtin_nontemporal_store(u, (w4*)((uint16_t*)p + i));
   } else {
     const w4 a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
@@ -108,12 +108,16 @@ __global__ void __launch_bounds__(256) k_gate(GateArgs a) {
   }
 }
 
-// Positions a thread walks (stride D): 16 for large calls, where fewer and
-// longer walks re-read less history; 8 for small ones (short prefill chunks,
-// decode), where more and shorter walks finish sooner (measured on MI355X).
-constexpr int conv_iters(int64_t n_tok) { return n_tok >= 16384 ? 16 : 8; }
+// Positions one walk visits (stride D), measured on MI355X inside the forward
+// pass: 16 for calls of at least 16384 tokens (B=8 T=4096: 8 -> 162 us,
+// 16 -> 142-154 us, 24 -> 169 us; B=1 T=32768 D=4: 262, 245-257, 265 us),
+// where longer walks re-read less history and reload the taps less often;
+// 8 for smaller calls, where more walks fill the GPU (B=4 T=1024: 11.7 us at 8,
+// 16.9 us at 16).
+constexpr int conv_walk(int64_t n_tok) { return n_tok >= 16384 ? 16 : 8; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 8 consecutive elements as raw words (bf16: one 16-byte piece in lo; f32:
 // two pieces, lo and hi)
@@ -144,114 +148,142 @@ __device__ __forceinline__ void unpack8(const u32x4& lo, const u32x4& hi, float 
   }
 }
 
+// 4 consecutive elements as raw words: 8 bytes of bf16 or 16 bytes of f32
+template <bool BF16>
+using Raw4 = typename std::conditional<BF16, u32x2, u32x4>::type;
+
+template <bool BF16>
+__device__ __forceinline__ void unpack4(const Raw4<BF16>& r, float scale, float* v) {
+  if constexpr (BF16) {
+    v[0] = __uint_as_float(r[0] << 16) * scale;
+    v[1] = __uint_as_float(r[0] & 0xFFFF0000u) * scale;
+    v[2] = __uint_as_float(r[1] << 16) * scale;
+    v[3] = __uint_as_float(r[1] & 0xFFFF0000u) * scale;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = __uint_as_float(r[k]) * scale;
+  }
+}
+
 // Workgroup order: workgroups are dispatched round-robin over the 8 XCDs, so
 // workgroup b runs on XCD b % 8; each XCD is given a contiguous range of
-// logical workgroups, and within it the channel block varies fastest.  The
-// workgroups of one output row (every branch of the same positions) then run
-// together on one XCD and read the row's value slices from that XCD's L2
-// instead of once per branch from memory.
+// logical workgroups.  Neighbouring logical workgroups then share one XCD's L2.
 __device__ __forceinline__ int xcd_contiguous(int bid, int total) {
   const int xcd = bid & 7, local = bid >> 3;
   const int per = total >> 3, rem = total & 7;
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-template <bool BF16, int KS, int kConvIters>
-__global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
-  const int groups = a.d >> 3;
-  const int cblocks = (a.hc * groups + 255) / 256;
-  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int gx = (L % cblocks) * 256 + threadIdx.x;
-  if (gx >= a.hc * groups) return;
-  const int h = gx / groups;
-  const int c0 = (gx - h * groups) * 8;
-  const int D = a.dil;
-  const int T = a.seqlen;
-  const int run_len = D * kConvIters;
-  const int runs = (T + run_len - 1) / run_len;
-  int y = L / cblocks;
-  const int r = y % D;
-  y /= D;
-  const int run = y % runs;
-  const int b = y / runs;
-  const int t_first = run * run_len + r;
-  if (t_first >= T) return;
-  const int n_it = min(kConvIters, (T - t_first + D - 1) / D);   // positions this thread visits
+// Gates are read through the constant address space: every lane of a
+// wavefront needs the same gate, which then comes through the scalar cache.
+// The gate arrays are not written while the conv runs.
+typedef const __attribute__((address_space(4))) float const_float;
 
+__device__ __forceinline__ const const_float* as_const(const float* p) { return (const const_float*)p; }
+
+// A wavefront takes one walk: positions t_first, t_first + D, ... (W of them)
+// of one residue mod D, over 256 consecutive channels (4 per lane), for every
+// branch.  Every conv tap of a position is either an earlier position of the
+// walk or one of the K-1 positions before it, so the walk loads those K-1 + W
+// value slices once, keeps them in registers, and then takes the branches one
+// after the other, each with its own taps (4 channels x K, reloaded per branch
+// from the cache) and gates.  The value rows are thus read once for all
+// branches instead of once per branch (B=8 T=4096 d=2560 hc=4, inside the
+// forward pass: 222 -> 142-154 us).  Positions before the call come from the
+// decode rings, or are zero before the sequence start.
+template <bool BF16, int KS, int W>
+__global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
+  constexpr int kCh = 4;              // channels per lane
+  constexpr int kWaveCh = 64 * kCh;   // channels per wavefront
+  constexpr int NP = KS - 1 + W;
+  constexpr int NH = KS > 1 ? KS - 1 : 1;
   const int64_t d = a.d;
-  const int R = (KS - 1) * D + 1;   // ring length of the state (history plus the slot a decode step fills)
+  const int D = a.dil, T = a.seqlen, hc = a.hc;
+  const int nch = (a.d + kWaveCh - 1) / kWaveCh;
+  const int runs = (T + W * D - 1) / (W * D);
+  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+  int w = __builtin_amdgcn_readfirstlane(L * 4 + (int)(threadIdx.x >> 6));
+  const int cc = w % nch;
+  w /= nch;
+  const int r = w % D;
+  w /= D;
+  const int run = w % runs;
+  const int b = w / runs;
+  const int c0 = cc * kWaveCh + (int)(threadIdx.x & 63) * kCh;
+  const int t_first = run * W * D + r;
+  if (b >= a.batch || t_first >= T || c0 >= a.d) return;
+  const int n_it = min(W, (T - t_first + D - 1) / D);   // positions of the walk inside the call
+  const int64_t R = (KS - 1) * D + 1;   // ring length of the state (history plus the slot a decode step fills)
   const int64_t past = a.n_past ? a.n_past[b] : 0;
 
-  // every V slice and gate of the walk is loaded before any is used, so a
-  // thread keeps up to kConvIters independent loads in flight
-  u32x4 lo[kConvIters], hi[kConvIters];
-  float gv[kConvIters];
+  // slot k holds position t_first + (k - (KS-1)) D: its raw value slice and
+  // its row of gates (null for a zero position)
+  Raw4<BF16> raw[NP];
+  const const_float* grow[NP];
 #pragma unroll
-  for (int it = 0; it < kConvIters; it++) {
-    lo[it] = hi[it] = u32x4{0, 0, 0, 0};
-    gv[it] = 0.f;
-    if (it < n_it) {
-      const int64_t n = (int64_t)b * T + t_first + it * D;
-      load_raw8<BF16>(a.v, n * a.v_stride + c0, lo[it], hi[it]);
-      gv[it] = a.g[n * a.hc + h];
+  for (int k = 0; k < NP; k++) {
+    const int t = t_first + (k - (KS - 1)) * D;
+    raw[k] = Raw4<BF16>{};
+    grow[k] = nullptr;
+    if (t >= 0) {
+      if (k - (KS - 1) < n_it) {
+        const int64_t n = (int64_t)b * T + t;
+        raw[k] = *(const Raw4<BF16>*)((const char*)a.v + (n * a.v_stride + c0) * (BF16 ? 2 : 4));
+        grow[k] = as_const(a.g + n * hc);
+      }
+    } else if (a.v_ring != nullptr && past + t >= 0) {
+      const int64_t slot = (int64_t)b * R + (past + t) % R;
+      raw[k] = *(const Raw4<BF16>*)((const char*)a.v_ring + (slot * d + c0) * (BF16 ? 2 : 4));
+      grow[k] = as_const(a.g_ring + slot * hc);
     }
   }
 
-  float w[KS][8];  // taps of channel c0+i: conv_w[h][c0+i][0..KS)
+#pragma unroll 1
+  for (int h = 0; h < hc; h++) {
+    // taps of channels c0..c0+3: conv_w[h][c0+i][0..KS), 4 KS consecutive
+    // elements, loaded 4 at a time (the array is 16-byte aligned and c0 % 4 == 0)
+    float wt[KS][kCh];
+    const int64_t e0 = ((int64_t)h * d + c0) * KS;
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+    for (int q = 0; q < KS; q++) {
+      float f[4];
+      unpack4<BF16>(*(const Raw4<BF16>*)((const char*)a.conv_w + (e0 + 4 * q) * (BF16 ? 2 : 4)), 1.f, f);
 #pragma unroll
-    for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
-
-  // gated value at a position before this walk's first one (from the rows of
-  // this call, the decode rings, or zero before the sequence start)
-  auto vg_before = [&](int t, float* out) {
-    if (t >= 0) {
-      const int64_t n = (int64_t)b * T + t;
-      u32x4 l, u;
-      load_raw8<BF16>(a.v, n * a.v_stride + c0, l, u);
-      unpack8<BF16>(l, u, a.g[n * a.hc + h], out);
-      return;
+      for (int m = 0; m < 4; m++) wt[(4 * q + m) % KS][(4 * q + m) / KS] = f[m];
     }
-    const int64_t p = past + t;
-    if (p < 0 || a.v_ring == nullptr) {
+    float hist[NH][kCh];
 #pragma unroll
-      for (int i = 0; i < 8; i++) out[i] = 0.f;
-      return;
-    }
-    const int64_t slot = (int64_t)b * R + p % R;
-    u32x4 l, u;
-    load_raw8<BF16>(a.v_ring, slot * d + c0, l, u);
-    unpack8<BF16>(l, u, a.g_ring[slot * a.hc + h], out);
-  };
-
-  // hist[j] = Vg at t - (KS-1-j) D for j < KS-1
-  constexpr int NH = KS > 1 ? KS - 1 : 1;
-  float hist[NH][8];
+    for (int k = 0; k < NP; k++) {
+      float cur[kCh];
+      unpack4<BF16>(raw[k], grow[k] != nullptr ? grow[k][h] : 0.f, cur);
+      const int it = k - (KS - 1);
+      if (it >= 0 && it < n_it) {
+        float out[kCh];
 #pragma unroll
-  for (int j = 0; j < KS - 1; j++) vg_before(t_first - (KS - 1 - j) * D, hist[j]);
-
+        for (int i = 0; i < kCh; i++) {
+          float acc = fmaf(wt[KS - 1][i], cur[i], cur[i]);
 #pragma unroll
-  for (int it = 0; it < kConvIters; it++) {
-    if (it >= n_it) continue;
-    const int t = t_first + it * D;
-    float cur[8], out[8];
-    unpack8<BF16>(lo[it], hi[it], gv[it], cur);
+          for (int j = 0; j < KS - 1; j++) acc = fmaf(wt[j][i], hist[j][i], acc);
+          out[i] = acc;
+        }
+        const int64_t o = (((int64_t)b * T + t_first + it * D) * hc + h) * d + c0;
+        if constexpr (BF16) {
+          const u32x2 u = {pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+          __builtin_nontemporal_store(u, (u32x2*)((uint16_t*)a.out + o));
+        } else {
+          const u32x4 u = {__float_as_uint(out[0]), __float_as_uint(out[1]), __float_as_uint(out[2]),
+                           __float_as_uint(out[3])};
+          __builtin_nontemporal_store(u, (u32x4*)((float*)a.out + o));
+        }
+      }
+      if constexpr (KS > 1) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      float acc = fmaf(w[KS - 1][i], cur[i], cur[i]);
+        for (int j = 0; j + 1 < NH; j++)
 #pragma unroll
-      for (int j = 0; j < KS - 1; j++) acc = fmaf(w[j][i], hist[j][i], acc);
-      out[i] = acc;
-    }
-    store8(a.out, (((int64_t)b * T + t) * a.hc + h) * d + c0, BF16, out);
-    if (KS > 1) {
+          for (int i = 0; i < kCh; i++) hist[j][i] = hist[j + 1][i];
 #pragma unroll
-      for (int j = 0; j + 1 < NH; j++)
-#pragma unroll
-        for (int i = 0; i < 8; i++) hist[j][i] = hist[j + 1][i];
-#pragma unroll
-      for (int i = 0; i < 8; i++) hist[NH - 1][i] = cur[i];
+        for (int i = 0; i < kCh; i++) hist[NH - 1][i] = cur[i];
+      }
     }
   }
 }
@@ -403,17 +435,17 @@ hipError_t decode_tail_dispatch(const DecodeTailArgs& a, dim3 grid, hipStream_t 
   return hipGetLastError();
 }
 
-template <bool BF16, int IT>
+template <bool BF16, int W>
 hipError_t conv_dispatch(const ConvArgs& a, dim3 grid, hipStream_t s) {
   switch (a.ksize) {
-    case 1: k_conv<BF16, 1, IT><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_conv<BF16, 2, IT><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_conv<BF16, 3, IT><<<grid, 256, 0, s>>>(a); break;
-    case 4: k_conv<BF16, 4, IT><<<grid, 256, 0, s>>>(a); break;
-    case 5: k_conv<BF16, 5, IT><<<grid, 256, 0, s>>>(a); break;
-    case 6: k_conv<BF16, 6, IT><<<grid, 256, 0, s>>>(a); break;
-    case 7: k_conv<BF16, 7, IT><<<grid, 256, 0, s>>>(a); break;
-    case 8: k_conv<BF16, 8, IT><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_conv<BF16, 1, W><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_conv<BF16, 2, W><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_conv<BF16, 3, W><<<grid, 256, 0, s>>>(a); break;
+    case 4: k_conv<BF16, 4, W><<<grid, 256, 0, s>>>(a); break;
+    case 5: k_conv<BF16, 5, W><<<grid, 256, 0, s>>>(a); break;
+    case 6: k_conv<BF16, 6, W><<<grid, 256, 0, s>>>(a); break;
+    case 7: k_conv<BF16, 7, W><<<grid, 256, 0, s>>>(a); break;
+    case 8: k_conv<BF16, 8, W><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -433,13 +465,16 @@ hipError_t launch_gate(const GateArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
-  if ((int64_t)a.batch * a.seqlen == 0) return hipSuccess;
-  const int lanes = a.hc * (a.d / 8);
-  const int it = conv_iters((int64_t)a.batch * a.seqlen);
-  const int run_len = a.dil * it;
-  const int runs = (a.seqlen + run_len - 1) / run_len;
-  dim3 grid((unsigned)((int64_t)a.batch * runs * a.dil * ((lanes + 255) / 256)));
-  if (it == 16) return a.bf16 ? conv_dispatch<true, 16>(a, grid, s) : conv_dispatch<false, 16>(a, grid, s);
+  const int64_t n_tok = (int64_t)a.batch * a.seqlen;
+  if (n_tok == 0) return hipSuccess;
+  if (a.dil < 1 || a.d % 8 != 0) return hipErrorInvalidValue;
+  // one wavefront per (sequence, run of W D positions, residue mod D, 256 channels)
+  const int W = conv_walk(n_tok);
+  const int64_t runs = (a.seqlen + (int64_t)W * a.dil - 1) / ((int64_t)W * a.dil);
+  const int64_t waves = (int64_t)a.batch * runs * a.dil * ((a.d + 255) / 256);
+  if ((waves + 3) / 4 > INT32_MAX / 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (W == 16) return a.bf16 ? conv_dispatch<true, 16>(a, grid, s) : conv_dispatch<false, 16>(a, grid, s);
   return a.bf16 ? conv_dispatch<true, 8>(a, grid, s) : conv_dispatch<false, 8>(a, grid, s);
 }
 

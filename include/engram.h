@@ -20,6 +20,9 @@
  *
  * Conventions for every call:
  *  - Array arguments are DEVICE pointers, allocated and owned by the caller.
+ *    tables, w_kv, gamma_k, gamma_q, conv_w, hidden, out, e and the value
+ *    ring are 16-byte aligned (ENGRAM_EINVAL otherwise); ids, remap, gates and
+ *    float32 gradient arrays need 4 bytes.
  *    The library allocates no memory and keeps no mutable global state; calls
  *    on different streams with disjoint outputs may run concurrently.
  *  - Calls validate their arguments on the host, enqueue kernels on `stream`

@@ -312,6 +312,27 @@ def test_chunked_prefill_matches_single_prefill(eg):
     assert st.n_past.cpu().tolist() == [c.T] * c.B
 
 
+def test_long_chunks_match_single_prefill(eg):
+    """Chunks of more than 16384 tokens each take the conv's long walks, whose
+    history at the chunk start comes from the state's rings; T = 2100 leaves a
+    ragged last run (walks cover 16 x 3 positions)."""
+    c = case("b4_t1024", batch=16, seqlen=2100)
+    full = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    st = eg.State(c.cfg(), c.B)
+    outs, t0 = [], 0
+    for L in (1040, 1060):
+        assert c.B * L >= 16384
+        ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+        hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+        outs.append(eg.forward(c.cfg(c.B, L), c.params, ids, hid, state=st))
+        t0 += L
+    sync()
+    assert torch.equal(torch.cat(outs, dim=1), full)
+    pos = c.sample_positions(256, seed=11)
+    err = normwise(to_f64(full).reshape(c.B * c.T, c.w.hc_mult, c.w.hidden)[pos], c.y_at_many(pos))
+    assert err <= TOL["bf16"], err
+
+
 def test_decode_matches_oracle(eg):
     """Decode-shaped workload: prompt prefill, then 512 single-token steps with
     state; for 8 seeded sequences every position's output must equal the

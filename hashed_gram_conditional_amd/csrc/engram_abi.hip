@@ -225,8 +225,8 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
 const char* const kForwardKernels[] = {"hash_gather", "project_gemm", "gate", "short_conv", "advance_state"};
 const char* const kFusedKernels[] = {"hash_gather", "project_gate_gemm", "gate_finalize", "short_conv",
                                      "advance_state"};
-const char* const kSplitKernels[] = {"hash_gather", "project_gate_gemm", "project_value_gemm", "gate_finalize",
-                                     "short_conv", "advance_state"};
+const char* const kSplitKernels[] = {"hash_gather", "project_gate_gemm", "project_value_gemm", "short_conv",
+                                     "advance_state"};
 const char* const kDecodeKernels[] = {"hash_gather", "project_gate_gemm", "decode_tail"};
 
 // A decode step (T = 1) with a state on the fused, unsplit projection ends in
@@ -401,12 +401,6 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
       if ((e = tm.before()) || (e = launch_decode_tail(dt, s)) || (e = tm.after())) return hip_status(e);
       return ENGRAM_OK;
     }
-    if (plan.split) {   // value channels: V = W_v e into the workspace
-      GemmArgs gv = gemm_args(c, p, e_rows, w.v);
-      gv.B = (const uint8_t*)p->w_kv + (int64_t)c->hc_mult * c->hidden * emb_dim(c) * esize(c);
-      gv.N = c->hidden;
-      if ((e = tm.before()) || (e = launch_gemm_bf16(gv, s)) || (e = tm.after())) return hip_status(e);
-    }
     GateFinalizeArgs gf;
     gf.partials = w.part;
     gf.g_out = w.g;
@@ -417,7 +411,14 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
     gf.eps = c->norm_eps;
     gf.clamp = c->gate_clamp;
     gf.inv_sqrt_d = (float)(1.0 / sqrt((double)c->hidden));
-    if ((e = tm.before()) || (e = launch_gate_finalize(gf, s)) || (e = tm.after())) return hip_status(e);
+    if (plan.split) {   // value channels: V = W_v e into the workspace, and the gates on the way
+      GemmArgs gv = gemm_args(c, p, e_rows, w.v);
+      gv.B = (const uint8_t*)p->w_kv + (int64_t)c->hc_mult * c->hidden * emb_dim(c) * esize(c);
+      gv.N = c->hidden;
+      if ((e = tm.before()) || (e = launch_gemm_bf16(gv, s, &gf)) || (e = tm.after())) return hip_status(e);
+    } else if ((e = tm.before()) || (e = launch_gate_finalize(gf, s)) || (e = tm.after())) {
+      return hip_status(e);
+    }
     v = w.v;
     v_stride = c->hidden;
   } else {
@@ -835,7 +836,7 @@ const char* engram_forward_kernel_name(const engram_config* cfg, int32_t with_st
   if (decode_tail_path(cfg, with_state != 0, false)) return i < 3 ? kDecodeKernels[i] : nullptr;
   const GatePlan plan = gate_plan(cfg);
   const char* const* names = plan.split ? kSplitKernels : plan.tile ? kFusedKernels : kForwardKernels;
-  const int n = (plan.split ? 6 : 5) - (with_state ? 0 : 1);   // advance_state is last
+  const int n = 5 - (with_state ? 0 : 1);   // advance_state is last
   return i < n ? names[i] : nullptr;
 }
 

@@ -111,6 +111,15 @@ hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool co
                               int max_blocks = 0);
 
 // ------------------------------------------------------------------ GEMM
+// g from the fused GEMM's partial sums (per token and branch, one float4 per
+// 128 channels)
+struct GateFinalizeArgs {
+  const float4* partials = nullptr;  // [N][hc][n_part]
+  float* g_out = nullptr;            // [N][hc]
+  int32_t n_tok = 0, hc = 0, d = 0, n_part = 0;
+  float eps = 0.f, clamp = 0.f, inv_sqrt_d = 0.f;
+};
+
 // C[M][N] = A[M][K] * B[N][K]^T (both operands K-contiguous), fp32 accumulate.
 struct GemmArgs {
   const void* A;   // e   [M][K]
@@ -126,7 +135,9 @@ struct GemmArgs {
 // split-K count for a float32-output product of M x N over a long K (1 = none)
 int gemm_k_splits(int64_t M, int64_t N, int64_t K);
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// fin: also form these gates (from partials complete before the launch), each
+// workgroup a share of them ahead of its K loop, so that no finalize kernel runs
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GateFinalizeArgs* fin = nullptr);
 // bf16 operands, float32 result stored or accumulated into C (a.accumulate)
 hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
@@ -143,6 +154,7 @@ struct GemmGateArgs {
   float4* partials;       // [M][hc][d/128]: per 128 channels x = sum K^2, y = sum Q^2, z = sum K gk gq Q
   int32_t hc, d;
   int32_t tile_n;         // channel tile: 256 or 128 (from gemm_gate_plan)
+  GateFinalizeArgs fin;   // plain GEMM only: gates to form ahead of the K loop (partials null: none)
 };
 
 // How the fused projection runs for M tokens: `tile` is its channel tile (0:
@@ -156,12 +168,6 @@ GatePlan gemm_gate_plan(int64_t M, int hc, int d);
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s);
 
 // g[n][h] from the partial sums of the fused GEMM
-struct GateFinalizeArgs {
-  const float4* partials;  // [N][hc][n_part]
-  float* g_out;            // [N][hc]
-  int32_t n_tok, hc, d, n_part;
-  float eps, clamp, inv_sqrt_d;
-};
 hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- gate / conv

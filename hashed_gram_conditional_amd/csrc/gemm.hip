@@ -376,6 +376,23 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (issue_all(std::integral_constant<int, I>{}), ...);
   }(std::make_integer_sequence<int, kStages - 1>{});
+  // a plain GEMM that follows the fused key projection forms the gates from
+  // its partial sums while the first operand steps are in flight; the loop
+  // bound depends on the workgroup only, so each 8-lane group stays whole
+  if constexpr (!GATE && !F32OUT) {
+    const GateFinalizeArgs& f = ga.fin;
+    if (f.partials != nullptr) {
+      constexpr int kGroups = 64 * NW / 8;
+      const int64_t n = (int64_t)f.n_tok * f.hc;
+      for (int64_t i0 = (int64_t)blockIdx.x * kGroups; i0 < n; i0 += (int64_t)gridDim.x * kGroups) {
+        const int64_t i = i0 + tid / 8;
+        const bool ok = i < n;
+        const float g = gate_from_partials8(f.partials + (ok ? i : 0) * f.n_part, f.n_part, ok, f.d, f.eps, f.clamp,
+                                            f.inv_sqrt_d);
+        if (ok && (tid & 7) == 0) f.g_out[i] = g;
+      }
+    }
+  }
   for (int kt = 0; kt < nk_pad; kt += kStages) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (step(std::integral_constant<int, I>{}, kt + I), ...);
@@ -633,10 +650,11 @@ static int pick_tile_n(int64_t M, int N) {
 }
 static bool few_tiles(int64_t M, int N) { return ((M + 127) / 128) * ((N + 127) / 128) <= 256; }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GateFinalizeArgs* fin) {
+  if (a.M == 0 || a.N == 0) return fin ? launch_gate_finalize(*fin, s) : hipSuccess;
   GemmGateArgs ga = {};
   ga.g = a;
+  if (fin) ga.fin = *fin;
   if (pick_tile_n(a.M, a.N) == 256) return gemm_launch<256, 256, 4, 2, 2, false>(ga, s);
   if (few_tiles(a.M, a.N)) return gemm_launch<128, 128, 2, 2, 4, false>(ga, s);
   return gemm_launch<128, 128, 2, 2, 2, false>(ga, s);

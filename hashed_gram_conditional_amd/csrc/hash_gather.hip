@@ -48,42 +48,56 @@ __device__ __forceinline__ uint32_t floored_mod(uint64_t u, uint32_t p, uint64_t
   return (uint32_t)r;
 }
 
-// Remapped ids of tokens n0-W .. n0+ntok-1 (W = max_order-1) into s_x; ids
-// before the start of the flattened batch read as pad.  Ends with a barrier.
-__device__ __forceinline__ void stage_window(const HashConsts& hc, const GatherArgs& a, int32_t* s_x, int64_t n0,
-                                             int ntok) {
+// Staging of one tile's tokens (ends with a barrier):
+//  - s_x: remapped ids of tokens n0-W .. n0+ntok-1 (W = max_order-1); ids before
+//    the start of the flattened batch read as pad;
+//  - s_hist[ti*W + k-1], for each token ti and offset k = 1..W that falls
+//    before its sequence's position 0: the compressed id there, from the
+//    state's token ring, or pad before the sequence start.
+// The ids (id, then remap) and the ring (n_past, then the ring slot) are each
+// two dependent loads; the first two waves take the ids and the last two the
+// ring, so the two chains overlap (one decode step: every token's history is
+// in the ring).
+__device__ __forceinline__ void stage_window(const HashConsts& hc, const GatherArgs& a, int32_t* s_x, int32_t* s_hist,
+                                             int64_t n0, int ntok) {
+  static_assert(kTokens + ENGRAM_MAX_ORDERS - 1 <= kThreads / 2 && kTokens * (ENGRAM_MAX_ORDERS - 1) <= kThreads / 2,
+                "one pass per half of the workgroup");
   const int W = hc.max_order - 1;
-  for (int i = threadIdx.x; i < ntok + W; i += kThreads) {
-    const int64_t n = n0 - W + i;
+  const int tid = threadIdx.x;
+  if (tid < ntok + W) {
+    const int64_t n = n0 - W + tid;
     int32_t x = hc.pad_id;
     if (n >= 0) {
       const int32_t id = a.ids[n];
       if (id >= 0 && id < hc.vocab) x = a.remap ? a.remap[id] : id;
     }
-    s_x[i] = x;
+    s_x[tid] = x;
+  }
+  const int j = tid - kThreads / 2;
+  if (j >= 0 && j < ntok * W) {
+    const int ti = j / W, k = 1 + j % W;
+    const int64_t n = n0 + ti, b = n / a.seqlen;
+    const int32_t t = (int32_t)(n - b * a.seqlen);
+    if (t - k < 0) {
+      const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
+      s_hist[j] = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
+    }
   }
   __syncthreads();
 }
 
 // Hash of token n = n0 + ti for head h with multipliers mult: the mix over the
 // order's shifted tokens (from the staged window, or before position 0 of the
-// sequence from the state's token ring, else pad), then the floored mod.
-__device__ __forceinline__ uint32_t hash_one(const HashConsts& hc, const GatherArgs& a, const int32_t* s_x, int64_t n0,
-                                             int ti, int h, const uint64_t* mult) {
+// sequence from the staged history), then the floored mod.
+__device__ __forceinline__ uint32_t hash_one(const HashConsts& hc, const GatherArgs& a, const int32_t* s_x,
+                                             const int32_t* s_hist, int64_t n0, int ti, int h, const uint64_t* mult) {
   const int W = hc.max_order - 1;
   const int64_t n = n0 + ti;
-  const int64_t b = n / a.seqlen;
-  const int32_t t = (int32_t)(n - b * a.seqlen);
+  const int32_t t = (int32_t)(n - n / a.seqlen * a.seqlen);
   const int order = hc.orders[h / hc.heads_per_order];
   uint64_t mix = 0;
   for (int k = 0; k < order; k++) {
-    int32_t tok;
-    if (t - k >= 0) {
-      tok = s_x[W + ti - k];
-    } else {
-      const int64_t p = (a.n_past ? a.n_past[b] : 0) + t - k;
-      tok = p < 0 ? hc.pad_id : a.tok_ring[b * W + p % W];
-    }
+    const int32_t tok = t - k >= 0 ? s_x[W + ti - k] : s_hist[ti * W + k - 1];
     mix ^= (uint64_t)(int64_t)tok * mult[k];
   }
   return floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
@@ -92,6 +106,7 @@ __device__ __forceinline__ uint32_t hash_one(const HashConsts& hc, const GatherA
 template <typename Chunk>
 __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherArgs a, int compute_hash) {
   __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
+  __shared__ int32_t s_hist[kTokens * ENGRAM_MAX_ORDERS];
   __shared__ int64_t s_row[kTokens * ENGRAM_MAX_HEADS];
 
   const int64_t N = (int64_t)a.batch * a.seqlen;
@@ -108,10 +123,10 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
           const int64_t n = n0 + ti, b = n / a.seqlen;
           if (n - b * a.seqlen == 0) a.past_out[b] = a.n_past ? a.n_past[b] : 0;
         }
-      stage_window(hc, a, s_x, n0, ntok);
+      stage_window(hc, a, s_x, s_hist, n0, ntok);
       for (int pr = tid; pr < ntok * H; pr += kThreads) {
         const int ti = pr / H, h = pr - ti * H;
-        const uint32_t r = hash_one(hc, a, s_x, n0, ti, h, hc.mult);
+        const uint32_t r = hash_one(hc, a, s_x, s_hist, n0, ti, h, hc.mult);
         if (a.idx_out) a.idx_out[(n0 + ti) * H + h] = (int32_t)r;
         s_row[ti * H + h] = hc.row_off[h] + r;
       }
@@ -156,17 +171,18 @@ __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherA
 // each (token, head) is hashed with every layer's multipliers.
 __global__ void __launch_bounds__(kThreads) k_hash_layers(HashConsts hc, LayerMults lm, GatherArgs a) {
   __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
+  __shared__ int32_t s_hist[kTokens * ENGRAM_MAX_ORDERS];
   const int64_t N = (int64_t)a.batch * a.seqlen;
   const int H = hc.n_heads;
   const int64_t n_tiles = (N + kTokens - 1) / kTokens;
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int64_t n0 = tile * kTokens;
     const int ntok = (int)min((int64_t)kTokens, N - n0);
-    stage_window(hc, a, s_x, n0, ntok);
+    stage_window(hc, a, s_x, s_hist, n0, ntok);
     for (int pr = threadIdx.x; pr < ntok * H; pr += kThreads) {
       const int ti = pr / H, h = pr - ti * H;
       for (int l = 0; l < lm.n_layers; l++)
-        a.idx_out[((int64_t)l * N + n0 + ti) * H + h] = (int32_t)hash_one(hc, a, s_x, n0, ti, h, lm.mult[l]);
+        a.idx_out[((int64_t)l * N + n0 + ti) * H + h] = (int32_t)hash_one(hc, a, s_x, s_hist, n0, ti, h, lm.mult[l]);
     }
     __syncthreads();   // s_x is rewritten by the next tile
   }

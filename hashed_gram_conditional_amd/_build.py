@@ -8,8 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libengram.so")
-SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gate_conv.hip", "backward.hip"]
-HEADERS = ["engram_internal.h", os.path.join("..", "..", "include", "engram.h")]
+SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gemm_tn.hip", "gate_conv.hip", "backward.hip"]
+HEADERS = ["engram_internal.h", "gemm_common.h", os.path.join("..", "..", "include", "engram.h")]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-shared", "-std=c++20", "-Wall",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -17,7 +17,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC
 
 
 # the sources the forward kernels are built from (the gradients' kernels are not among them)
-FORWARD_SOURCES = [f for f in SOURCES if f != "backward.hip"]
+FORWARD_SOURCES = [f for f in SOURCES if f not in ("backward.hip", "gemm_tn.hip")]
 
 
 def source_hash() -> str:

@@ -163,8 +163,9 @@ Workspace carve(const engram_config* c, void* base) {
 }
 
 // Workspace of engram_backward: the forward quantities it recomputes, the
-// gradients between steps, and the transposed GEMM operands (token axis
-// padded to a multiple of 64 with zeros).
+// gradients between steps and, where dW cannot read dkv and e as stored
+// (float32, or chunks past 32-bit buffer offsets), their transposed copies
+// (token axis padded to a multiple of 64 with zeros).
 struct BwdWorkspace {
   void* e;          // [N][E]
   int32_t* idx;     // [N][H]
@@ -176,8 +177,8 @@ struct BwdWorkspace {
   void* dkv;        // [N][hc+1][d]
   float* de;        // [N][E]
   void* wT;         // [E][(hc+1)d]
-  void* dkvT;       // [S][(hc+1)d][Np/S]: token axis in S split-K chunks
-  void* eT;         // [S][E][Np/S]
+  void* dkvT;       // [S][(hc+1)d][Np/S]: token axis in S split-K chunks (null when dW reads dkv and e as stored)
+  void* eT;         // [S][E][Np/S] (null alike)
   float* wpart;     // [S][(hc+1)d][E] when S > 1: the splits' products
   float* gpart;     // [gate_bwd_rows(N)][hc][d]: per-block sums for the gammas' gradients
   float* cpart;     // [conv_bwd_rows][hc][d][K]: per-block sums for the taps' gradients
@@ -186,6 +187,25 @@ struct BwdWorkspace {
   int S;
   size_t bytes;
 };
+
+// dW = dKV^T e over the token axis, in `splits` chunks of Ks tokens, read from
+// dkv [N][(hc+1)d] and e [N][E] as stored (bf16 path)
+GemmTnArgs dw_args(const engram_config* c, const void* dkv, const void* e, float* out, int splits, int64_t Ks) {
+  GemmTnArgs g;
+  g.A = dkv;
+  g.B = e;
+  g.C = out;
+  g.M = (int32_t)((int64_t)(c->hc_mult + 1) * c->hidden);
+  g.N = (int32_t)emb_dim(c);
+  g.K = (int64_t)c->batch * c->seqlen;
+  g.Ks = Ks;
+  g.lda = g.M;
+  g.ldb = g.N;
+  g.splits = splits;
+  g.split_c = (int64_t)g.M * g.N;
+  g.accumulate = splits > 1 ? 0 : 1;
+  return g;
+}
 
 BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   const int64_t N = (int64_t)c->batch * c->seqlen, E = emb_dim(c), O = (int64_t)(c->hc_mult + 1) * c->hidden;
@@ -212,8 +232,10 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.dkv = take((size_t)(N * O * es));
   w.de = (float*)take((size_t)(N * E) * sizeof(float));
   w.wT = take((size_t)(E * O * es));
-  w.dkvT = take((size_t)(O * w.Np * es));
-  w.eT = take((size_t)(E * w.Np * es));
+  if (c->dtype != ENGRAM_BF16 || !gemm_tn_fits(dw_args(c, nullptr, nullptr, nullptr, w.S, w.Ks))) {
+    w.dkvT = take((size_t)(O * w.Np * es));
+    w.eT = take((size_t)(E * w.Np * es));
+  }
   w.wpart = w.S > 1 ? (float*)take((size_t)w.S * O * E * sizeof(float)) : nullptr;
   w.gpart = (float*)take((size_t)gate_bwd_rows(N) * c->hc_mult * c->hidden * sizeof(float));
   w.cpart = (float*)take((size_t)conv_bwd_rows(c->batch, c->seqlen) * c->hc_mult * c->hidden * c->conv_kernel *
@@ -576,6 +598,13 @@ engram_status gradients(const engram_config* cfg, const engram_params* prm, cons
   // dW += dKV^T e
   // (in S split-K chunks of the token axis when the output has too few tiles
   // to fill the chip; the chunks' products are then added in chunk order)
+  if (w.dkvT == nullptr) {   // bf16: the operands as stored, through transposing LDS reads
+    const GemmTnArgs g2 = dw_args(cfg, w.dkv, w.e, w.S > 1 ? w.wpart : d_w_kv, w.S, w.Ks);
+    if ((e = launch_gemm_tn_bf16_f32out(g2, stream))) return hip_status(e);
+    if (w.S > 1 && (e = launch_colsum(w.wpart, w.S, O * E, d_w_kv, nullptr, nullptr, nullptr, bf16, stream)))
+      return hip_status(e);
+    return ENGRAM_OK;
+  }
   const int64_t chunk = w.S > 1 ? w.Ks : 0;
   if ((e = launch_transpose(w.dkv, w.dkvT, N, O, w.Np, es, stream, chunk))) return hip_status(e);
   if ((e = launch_transpose(w.e, w.eT, N, E, w.Np, es, stream, chunk))) return hip_status(e);

@@ -140,6 +140,25 @@ int gemm_k_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GateFinalizeArgs* fin = nullptr);
 // bf16 operands, float32 result stored or accumulated into C (a.accumulate)
 hipError_t launch_gemm_bf16_f32out(const GemmArgs& a, hipStream_t s);
+
+// C[M][N] (float32) = sum_k A[k][m] B[k][n] over bf16 operands stored
+// reduction-major (row k holds every m, resp. every n), in `splits` chunks of
+// Ks rows: chunk s reduces rows [s Ks, min((s+1) Ks, K)) into C + s split_c.
+struct GemmTnArgs {
+  const void* A;        // [K][lda]
+  const void* B;        // [K][ldb]
+  float* C;             // [splits][M][N]
+  int32_t M, N;
+  int64_t K, Ks;        // rows in all, rows per chunk (a multiple of 64)
+  int64_t lda, ldb;     // elements, multiples of 8
+  int32_t splits = 1;
+  int64_t split_c = 0;
+  int32_t accumulate = 0;   // C += instead of C =
+};
+// false when the shapes leave the kernel's 32-bit buffer offsets (then use
+// launch_gemm_bf16_f32out on transposed copies)
+bool gemm_tn_fits(const GemmTnArgs& a);
+hipError_t launch_gemm_tn_bf16_f32out(const GemmTnArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 // Projection GEMM with the gate reductions in its epilogue (bf16).  Key tiles

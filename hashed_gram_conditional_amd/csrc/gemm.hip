@@ -24,15 +24,10 @@
 
 #include <algorithm>
 
-#include "engram_internal.h"
+#include "gemm_common.h"
 
 namespace engram {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 
 #ifndef ENGRAM_GEMM_BK
 #define ENGRAM_GEMM_BK 64
@@ -40,8 +35,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BK = ENGRAM_GEMM_BK;           // reduction step (bf16 elements)
 constexpr int kPieces = BK / 8;              // 16-byte pieces per LDS row
 constexpr int kRowsPerDma = 64 / kPieces;    // rows one 1 KB DMA instruction fills
-
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Physical 16-byte piece of logical piece `piece` in LDS row `row`.  LDS reads
 // are served 256 bytes (64 banks) at a time, i.e. 16 lanes of a ds_read_b128;
@@ -53,25 +46,6 @@ __device__ __forceinline__ int swz(int row, int piece) {
   else return piece ^ ((row >> 2) & 3);                          // 64-byte rows: 4 rows per bank line
 }
 
-// Logical tile of a workgroup.  Workgroups are dispatched round-robin over the
-// 8 XCDs, so workgroup b runs on XCD b % 8; each XCD is given a contiguous
-// range of logical tiles, ordered GROUP m-tiles at a time with the channel
-// tiles innermost, so the tiles resident on one XCD share a few token slabs
-// and weight slabs in that XCD's L2.
-__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& mt, int& nt) {
-  constexpr int GROUP = 4;
-  const int total = m_tiles * n_tiles;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int L = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int span = GROUP * n_tiles;
-  const int first_m = (L / span) * GROUP;
-  const int gsz = min(m_tiles - first_m, GROUP);
-  const int r = L - (L / span) * span;
-  mt = first_m + r % gsz;
-  nt = r / gsz;
-}
-
 // Buffer resource over rows [row0, row0 + rows) of a K-contiguous bf16 matrix:
 // loads past the last valid row, or at an offset marked out of range, return
 // zero, so ragged tiles and the K tail need no branches.
@@ -80,12 +54,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * K), (short)0, (int)(bytes > 0 ? bytes : 0),
                                            0x00020000);
 }
-
-constexpr int kOutOfRange = (int)0x80000000;
-
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
-// bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 

@@ -95,6 +95,21 @@ def test_backward_matches_oracle(eg, name, over):
         assert normwise(got[k], ref[k]) <= TOL[c.w.dtype], (k, normwise(got[k], ref[k]))
 
 
+def test_weight_gradient_in_large_tiles(eg):
+    """The weight gradient's GEMM in its 256 x 256 tiles, which it takes from
+    512 tiles on: hidden 4096 with one branch (8192 channels) by 32 heads of 128
+    (E = 4096) give 32 x 16 tiles from only 16 tokens; every gradient against
+    the oracle."""
+    c = Case("b4_t1024", batch=1, seqlen=16, prime_base=4001, hidden=4096, hc_mult=1, heads_per_order=16,
+             head_dim=128)
+    assert (c.w.hc_mult + 1) * c.w.hidden // 256 * (c.w.emb_dim // 256) >= 512
+    hid = _aligned_hidden(c, seed=9)
+    got, ref, _ = _run(eg, c, hid, seed=23)
+    for k in NAMES:
+        assert np.abs(ref[k]).max() > 0, k
+        assert normwise(got[k], ref[k]) <= TOL[c.w.dtype], (k, normwise(got[k], ref[k]))
+
+
 @pytest.mark.parametrize("name,over", CASES[:2])
 def test_backward_generic_inputs(eg, name, over):
     c = Case(name, **over)

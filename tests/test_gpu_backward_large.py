@@ -10,7 +10,8 @@ Gradients through the gate's score are compared where |s| >= 0.05 for the
 tokens involved: the slope 1/(2 sqrt|s|) amplifies the rounding of s without
 bound as s nears 0.  The weight, gamma and tap gradients are sums over the
 whole batch; at this size they are checked by exact linearity in dy and by
-the saved-activation path giving the same bits."""
+the saved-activation path giving the same bits, and the weight gradient also
+by an identity that ties it to the table rows' gradient."""
 import concurrent.futures
 import multiprocessing
 
@@ -170,3 +171,30 @@ def test_saved_activations_give_the_same_gradients(eg, case, run):
         assert torch.equal(g2[k], grads[k]), k
     t1, t2 = grads["d_tables"], g2["d_tables"]
     assert (t2 - t1).abs().max().item() <= 1e-6 * t1.abs().max().item()
+
+
+def _dot64(a, b, rows=1 << 20):
+    """sum of a * b in float64, over row chunks (the tables are 3 GB in bf16)"""
+    tot = torch.zeros((), dtype=torch.float64, device="cuda")
+    for i in range(0, a.shape[0], rows):
+        tot += (a[i:i + rows].double() * b[i:i + rows].double()).sum()
+    return tot.item()
+
+
+def test_weight_and_table_gradients_agree(eg, case):
+    """<W_kv, dW_kv> = <tables, d_tables>: both are sum_t <dKV[t], W e[t]>.
+    dW = sum_t dKV[t]^T e[t] comes from the weight GEMM over the token axis
+    (here in split-K chunks), the table rows' gradient from de = dKV W
+    scattered to the rows e came from: two independent paths.  With dy = y
+    the sum is |y|^2 up to the epsilon of the key norm (y is linear in V, and
+    the gates do not change when K is scaled), so it is large and positive and
+    a wrong weight gradient cannot hide in cancellation."""
+    c = case
+    y = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    _, g = eg.backward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"], y)
+    torch.cuda.synchronize()
+    yy = _dot64(y.reshape(-1, c.w.hidden), y.reshape(-1, c.w.hidden))
+    lhs = _dot64(c.dev["w_kv"], g["d_w_kv"])
+    rhs = _dot64(c.dev["tables"], g["d_tables"])
+    assert lhs > 0.5 * yy, (lhs, yy)
+    assert abs(lhs - rhs) <= 1e-3 * abs(lhs), (lhs, rhs, yy)

@@ -97,6 +97,13 @@ def test_forward_rejects_short_workspace_and_null_pointers(eg):
                               None) == -1
     # misaligned device pointers
     assert lib.engram_forward(ctypes.byref(c), ctypes.byref(prm), P(16), P(18), None, P(16), P(256), ws, None) == -1
+    # every parameter array but remap is 16-byte aligned (the conv taps are read 8 or 16 bytes at a time)
+    for i in range(1, 6):
+        args = [P(16)] * 6
+        args[i] = P(16 + 4)
+        bad = eg._Params(*args)
+        assert lib.engram_forward(ctypes.byref(c), ctypes.byref(bad), P(16), P(16), None, P(16), P(256), ws,
+                                  None) == -1, i
 
 
 def test_empty_calls_succeed_without_launching(eg):

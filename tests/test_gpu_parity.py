@@ -252,6 +252,8 @@ def test_forward_within_tolerance(eg, name, n):
     (dict(batch=3, seqlen=77, hidden=256, hc_mult=2), True),     # fused GEMM with a ragged token count
     (dict(batch=1, seqlen=300, hidden=384, hc_mult=1, orders=[2, 3, 4], conv_dilation=4), True),
     (dict(batch=2, seqlen=2000), True),   # key channels 256-wide, then the value channels as a plain GEMM
+    (dict(batch=1, seqlen=130, hidden=96, hc_mult=8), False),    # 8 branches; 24 of a wavefront's 64 lanes in the conv
+    (dict(batch=2, seqlen=61, hidden=256, hc_mult=6, conv_kernel=3, conv_dilation=2), True),   # 6 branches
 ])
 def test_forward_paths_on_ragged_shapes(eg, over, fused):
     c = case("b4_t1024", **over)

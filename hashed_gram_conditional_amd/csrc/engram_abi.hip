@@ -171,6 +171,7 @@ struct BwdWorkspace {
   int32_t* idx;     // [N][H]
   void* kv;         // [N][hc+1][d]
   float4* stats;    // [N][hc] (g, s, rk, rq)
+  float4* part;     // [N][hc][d/128]: the fused projection's gate sums (when the fused plan applies)
   float* g;         // [N][hc] gates (the conv of engram_forward_train reads them)
   void* dvg;        // [N][hc][d] dtype: gradient of the gated values (hc not a power of two)
   float* dgp;       // [N][n_dgp][hc]: dg partials of the fused conv kernel (hc a power of two)
@@ -224,6 +225,7 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.idx = (int32_t*)take((size_t)N * n_heads(c) * sizeof(int32_t));
   w.kv = take((size_t)(N * O * es));
   w.stats = (float4*)take((size_t)N * c->hc_mult * sizeof(float4));
+  if (fused_tile(c)) w.part = (float4*)take((size_t)N * c->hc_mult * (c->hidden / 128) * sizeof(float4));
   w.g = (float*)take((size_t)N * c->hc_mult * sizeof(float));
   if (conv_bwd_fused(c->hc_mult))
     w.dgp = (float*)take((size_t)N * c->hc_mult * conv_bwd_dg_parts(c->hc_mult, c->hidden) * sizeof(float));
@@ -515,11 +517,49 @@ hipError_t forward_quantities(const engram_config* cfg, const engram_params* prm
   ga.idx_out = w.idx;
   ga.e_out = (uint8_t*)w.e;
   if ((e = launch_hash_gather(hc, ga, true, stream, gather_grid_cap(prm->tables)))) return e;
-  const GemmArgs gm = gemm_args(cfg, prm, w.e, w.kv);
-  if ((e = bf16 ? launch_gemm_bf16(gm, stream) : launch_gemm_f32(gm, stream))) return e;
-  GateArgs gt = gate_args(cfg, prm, w.kv, hidden, w.g);
-  gt.stats = w.stats;
-  return launch_gate(gt, stream);
+  const GatePlan plan = gate_plan(cfg);
+  if (w.part == nullptr) {   // K/V stored, then the gate statistics from them
+    const GemmArgs gm = gemm_args(cfg, prm, w.e, w.kv);
+    if ((e = bf16 ? launch_gemm_bf16(gm, stream) : launch_gemm_f32(gm, stream))) return e;
+    GateArgs gt = gate_args(cfg, prm, w.kv, hidden, w.g);
+    gt.stats = w.stats;
+    return launch_gate(gt, stream);
+  }
+  // the fused projection as in engram_forward, with the keys stored as well,
+  // and the statistics formed from its sums
+  const int64_t hcd = (int64_t)cfg->hc_mult * cfg->hidden, O = hcd + cfg->hidden;
+  GemmGateArgs gg;
+  gg.g = gemm_args(cfg, prm, w.e, nullptr);
+  gg.hidden = hidden;
+  gg.gamma_k = prm->gamma_k;
+  gg.gamma_q = prm->gamma_q;
+  gg.v_out = (uint8_t*)w.kv + hcd * esize(cfg);
+  gg.v_ld = O;
+  gg.k_out = w.kv;
+  gg.k_ld = O;
+  gg.partials = w.part;
+  gg.hc = cfg->hc_mult;
+  gg.d = cfg->hidden;
+  gg.tile_n = plan.tile;
+  if (plan.split) gg.g.N = (int32_t)hcd;
+  if ((e = launch_gemm_gate_bf16(gg, stream))) return e;
+  GateFinalizeArgs gf;
+  gf.partials = w.part;
+  gf.g_out = w.g;
+  gf.stats = w.stats;
+  gf.n_tok = (int32_t)((int64_t)cfg->batch * cfg->seqlen);
+  gf.hc = cfg->hc_mult;
+  gf.d = cfg->hidden;
+  gf.n_part = cfg->hidden / 128;
+  gf.eps = cfg->norm_eps;
+  gf.clamp = cfg->gate_clamp;
+  gf.inv_sqrt_d = (float)(1.0 / sqrt((double)cfg->hidden));
+  if (!plan.split) return launch_gate_finalize(gf, stream);
+  GemmArgs gv = gemm_args(cfg, prm, w.e, (uint8_t*)w.kv + hcd * esize(cfg));
+  gv.B = (const uint8_t*)prm->w_kv + hcd * emb_dim(cfg) * esize(cfg);
+  gv.N = cfg->hidden;
+  gv.ldc = O;
+  return launch_gemm_bf16(gv, stream, &gf);
 }
 
 // Gradients from the forward quantities in the workspace.

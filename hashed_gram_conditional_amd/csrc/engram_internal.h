@@ -36,7 +36,7 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool bf16) {
 // g): rk = (sum K^2 / d + eps)^-1/2, rq alike, s = (sum K gk gq Q) rk rq / sqrt(d),
 // g = sigmoid(sign(s) sqrt(max(|s|, clamp))).  All 8 lanes must call it.
 __device__ __forceinline__ float gate_from_partials8(const float4* p, int n_part, bool ok, int d, float eps,
-                                                     float clamp, float inv_sqrt_d) {
+                                                     float clamp, float inv_sqrt_d, float4* st = nullptr) {
   const int l = threadIdx.x & 7;
   float kk = 0.f, qq = 0.f, kq = 0.f;
   if (ok)
@@ -58,7 +58,9 @@ __device__ __forceinline__ float gate_from_partials8(const float4* p, int n_part
   const float s = kq * rk * rq * inv_sqrt_d;
   const float sgn = s > 0.f ? 1.f : (s < 0.f ? -1.f : 0.f);
   const float act = sgn * sqrtf(fmaxf(fabsf(s), clamp));
-  return 1.f / (1.f + expf(-act));
+  const float g = 1.f / (1.f + expf(-act));
+  if (st) *st = make_float4(g, s, rk, rq);   // the statistics the gradients read
+  return g;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -116,6 +118,7 @@ hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool co
 struct GateFinalizeArgs {
   const float4* partials = nullptr;  // [N][hc][n_part]
   float* g_out = nullptr;            // [N][hc]
+  float4* stats = nullptr;           // [N][hc] (g, s, rk, rq), or null
   int32_t n_tok = 0, hc = 0, d = 0, n_part = 0;
   float eps = 0.f, clamp = 0.f, inv_sqrt_d = 0.f;
 };
@@ -124,8 +127,9 @@ struct GateFinalizeArgs {
 struct GemmArgs {
   const void* A;   // e   [M][K]
   const void* B;   // w_kv [N][K]
-  void* C;         // kv  [M][N]
+  void* C;         // kv  [M][ldc]
   int32_t M, N, K;
+  int64_t ldc = 0;  // bf16 output's row stride in elements (0: N)
   int32_t accumulate = 0;   // float32 outputs: C += A B^T instead of C = A B^T
   // float32 outputs only: `splits` independent products in one launch, the
   // s-th on A + s split_a, B + s split_b into C + s split_c (elements)
@@ -169,10 +173,13 @@ struct GemmGateArgs {
   const void* hidden;     // [M][hc][d] queries
   const void* gamma_k;    // [hc][d]
   const void* gamma_q;    // [hc][d]
-  void* v_out;            // [M][d]
+  void* v_out;            // [M][v_ld]
   float4* partials;       // [M][hc][d/128]: per 128 channels x = sum K^2, y = sum Q^2, z = sum K gk gq Q
   int32_t hc, d;
   int32_t tile_n;         // channel tile: 256 or 128 (from gemm_gate_plan)
+  int64_t v_ld = 0;       // row stride of v_out in elements (0: d)
+  void* k_out = nullptr;  // [M][k_ld], the keys in columns 0 .. hc d - 1, or null (not stored)
+  int64_t k_ld = 0;
   GateFinalizeArgs fin;   // plain GEMM only: gates to form ahead of the K loop (partials null: none)
 };
 

@@ -87,6 +87,7 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // one wave's loads and barrier overlap the other wave's MFMAs.
 //
 // GATE = false: the tile is stored to C (bf16).
+// STORE_K (with GATE): key tiles are also stored, to k_out (the gradients read them).
 // GATE = true (fused gate): a tile of branch h's key channels is not stored;
 // its epilogue reads the matching tile of the hidden state Q (the query of
 // branch h) and the two RMSNorm scales, and writes per token and 128 channels
@@ -95,7 +96,7 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // the scaled dot of RMSNorm(K) and RMSNorm(Q), and RMSNorm only needs the mean
 // square).  Value tiles are stored to v_out.  Writing K and reading it back
 // is the largest traffic of the unfused path.
-template <int BM, int BN, int WM, int WN, int kStages, bool GATE, bool F32OUT = false>
+template <int BM, int BN, int WM, int WN, int kStages, bool GATE, bool F32OUT = false, bool STORE_K = false>
 __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) {
   constexpr int NW = WM * WN;                          // waves
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // MFMA tiles per wave along tokens / channels
@@ -355,9 +356,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
       for (int64_t i0 = (int64_t)blockIdx.x * kGroups; i0 < n; i0 += (int64_t)gridDim.x * kGroups) {
         const int64_t i = i0 + tid / 8;
         const bool ok = i < n;
+        float4 st;
         const float g = gate_from_partials8(f.partials + (ok ? i : 0) * f.n_part, f.n_part, ok, f.d, f.eps, f.clamp,
-                                            f.inv_sqrt_d);
-        if (ok && (tid & 7) == 0) f.g_out[i] = g;
+                                            f.inv_sqrt_d, &st);
+        if (ok && (tid & 7) == 0) {
+          f.g_out[i] = g;
+          if (f.stats) f.stats[i] = st;
+        }
       }
     }
   }
@@ -421,12 +426,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
         }
     }
   } else if constexpr (!GATE) {
-    store_tile((uint16_t*)a.C, a.N, n0, a.N);
+    store_tile((uint16_t*)a.C, a.ldc ? a.ldc : a.N, n0, a.N);
   } else {
     const int d = ga.d, hc = ga.hc;
     const int h = (int)(n0 / d);
     if (h >= hc) {  // value tile
-      store_tile((uint16_t*)ga.v_out, d, n0 - (int64_t)hc * d, d);
+      store_tile((uint16_t*)ga.v_out, ga.v_ld ? ga.v_ld : d, n0 - (int64_t)hc * d, d);
       return;
     }
     // key tile of branch h: channels c0 .. c0+BN-1 of the branch
@@ -518,6 +523,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
                 make_float4(kk[0][j] + kk[1][j], qq[0][j] + qq[1][j], kq[0][j] + kq[1][j], 0.f);
         }
       }
+      if constexpr (STORE_K) store_tile((uint16_t*)ga.k_out, ga.k_ld, n0, (int64_t)hc * d);
       return;
     }
     // the WN waves of a token row meet in LDS; the operand stages are free now
@@ -545,6 +551,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
         ga.partials[(m * hc + h) * n_part + part] = o;
       }
     }
+    if constexpr (STORE_K) store_tile((uint16_t*)ga.k_out, ga.k_ld, n0, (int64_t)hc * d);
   }
 }
 
@@ -553,9 +560,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
 __global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
   const bool ok = i < (int64_t)a.n_tok * a.hc;
+  float4 st;
   const float g = gate_from_partials8(a.partials + (ok ? i : 0) * a.n_part, a.n_part, ok, a.d, a.eps, a.clamp,
-                                      a.inv_sqrt_d);
-  if (ok && (threadIdx.x & 7) == 0) a.g_out[i] = g;
+                                      a.inv_sqrt_d, &st);
+  if (ok && (threadIdx.x & 7) == 0) {
+    a.g_out[i] = g;
+    if (a.stats) a.stats[i] = st;
+  }
 }
 
 // float32 path: a plain LDS-tiled FMA GEMM, 64x64 tile, 4x4 outputs per thread.
@@ -599,10 +610,10 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int ST, bool GATE, bool F32OUT = false>
+template <int BM, int BN, int WM, int WN, int ST, bool GATE, bool F32OUT = false, bool STORE_K = false>
 hipError_t gemm_launch(const GemmGateArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)a.g.splits * ((a.g.M + BM - 1) / BM) * ((a.g.N + BN - 1) / BN);
-  k_gemm_bf16<BM, BN, WM, WN, ST, GATE, F32OUT><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
+  k_gemm_bf16<BM, BN, WM, WN, ST, GATE, F32OUT, STORE_K><<<(unsigned)tiles, 64 * WM * WN, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -693,6 +704,12 @@ GatePlan gemm_gate_plan(int64_t M, int hc, int d) {
 hipError_t launch_gemm_gate_bf16(const GemmGateArgs& a, hipStream_t s) {
   if (a.g.M == 0 || a.g.N == 0) return hipSuccess;
   const int bn = a.tile_n;
+  if (a.k_out != nullptr) {   // the keys stored as well (training)
+    if (bn == 256) return gemm_launch<256, 256, 4, 2, 2, true, false, true>(a, s);
+    if (bn == 128 && few_tiles(a.g.M, a.g.N)) return gemm_launch<128, 128, 2, 2, 4, true, false, true>(a, s);
+    if (bn == 128) return gemm_launch<128, 128, 2, 2, 2, true, false, true>(a, s);
+    return hipErrorInvalidValue;
+  }
   if (bn == 256) return gemm_launch<256, 256, 4, 2, 2, true>(a, s);
   if (bn == 128 && few_tiles(a.g.M, a.g.N)) return gemm_launch<128, 128, 2, 2, 4, true>(a, s);
   if (bn == 128) return gemm_launch<128, 128, 2, 2, 2, true>(a, s);

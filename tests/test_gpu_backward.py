@@ -135,16 +135,20 @@ def test_backward_accumulates(eg):
     assert torch.equal(dh2, dh)
 
 
-@pytest.mark.parametrize("name,over", [("tiny_fp32", {}), ("b4_t1024", dict(batch=2, seqlen=200, prime_base=4001))])
-def test_forward_train_matches_oracle(eg, name, over):
-    """engram_forward_train's output, at every position, within the dtype's bar."""
+@pytest.mark.parametrize("name,over,n", [("tiny_fp32", {}, None),
+                                         ("b4_t1024", dict(batch=2, seqlen=200, prime_base=4001), None),
+                                         ("b4_t1024", {}, 256)])
+def test_forward_train_matches_oracle(eg, name, over, n):
+    """engram_forward_train's output within the dtype's bar: at every position,
+    or (B=4 T=1024, where the key channels and the value channels are two
+    GEMMs) at 256 seeded positions and the sequence-start edge."""
     c = Case(name, **over)
     ws = eg.alloc_backward_workspace(c.cfg())
     y = eg.forward_train(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"], ws)
     torch.cuda.synchronize()
     N = c.B * c.T
-    pos = np.arange(N)
-    got = y.to(torch.float64).cpu().numpy().reshape(N, c.w.hc_mult, c.w.hidden)
+    pos = np.arange(N) if n is None else c.sample_positions(n, seed=4)
+    got = y.to(torch.float64).cpu().numpy().reshape(N, c.w.hc_mult, c.w.hidden)[pos]
     assert normwise(got, c.y_at_many(pos)) <= TOL[c.w.dtype]
 
 

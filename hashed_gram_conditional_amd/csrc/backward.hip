@@ -55,13 +55,6 @@ __device__ __forceinline__ void st8(void* p, int64_t i, bool bf16, const float* 
   }
 }
 
-// 8 consecutive values at element i, or zeros when !ok (address clamped to 0)
-__device__ __forceinline__ void ld8_or0(const void* p, int64_t i, bool ok, bool bf16, float* v) {
-  ld8(p, ok ? i : 0, bf16, v);
-#pragma unroll
-  for (int k = 0; k < 8; k++) v[k] = ok ? v[k] : 0.f;
-}
-
 // 4 consecutive values at element i as floats, zeros when !ok (address clamped to 0)
 __device__ __forceinline__ void ld4_or0(const void* p, int64_t i, bool ok, bool bf16, float* v) {
   if (bf16) {

@@ -50,6 +50,7 @@ engram_status validate(const engram_config* c) {
 }
 
 engram_status check_params(const engram_config* c, const engram_params* p) {
+  (void)c;
   if (p == nullptr || p->tables == nullptr || p->w_kv == nullptr || p->gamma_k == nullptr ||
       p->gamma_q == nullptr || p->conv_w == nullptr)
     return ENGRAM_EINVAL;

@@ -358,7 +358,7 @@ __global__ void __launch_bounds__(256) k_decode_tail(DecodeTailArgs a) {
   const int64_t d = a.d, R = a.ring_len;
   const int64_t new_slot = (int64_t)b * R + past % R;
 
-  if (threadIdx.x < 8 * nb) {   // whole 8-lane groups
+  if ((int)threadIdx.x < 8 * nb) {   // whole 8-lane groups
     const int hb = threadIdx.x >> 3, hh = h_lo + hb;
     const float g = gate_from_partials8(a.partials + ((int64_t)b * a.hc + hh) * a.n_part, a.n_part, true, a.d,
                                         a.eps, a.clamp, a.inv_sqrt_d);

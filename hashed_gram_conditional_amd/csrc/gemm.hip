@@ -380,6 +380,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   auto store_tile = [&](uint16_t* __restrict__ C, int64_t ldc, int64_t col0, int64_t ncols) {
     constexpr int RP = BN / 8;        // 16-byte pieces per tile row
     constexpr int RPI = 64 / RP;      // tile rows per wave instruction
+    static_assert(BM % (NW * RPI) == 0, "whole store rounds");
     uint16_t* t = reinterpret_cast<uint16_t*>(&smem[0]);
     __syncthreads();                  // every wave is done with the operand stages
 #pragma unroll
@@ -397,8 +398,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
     }
     __syncthreads();
 #pragma unroll
-    for (int r0 = wave * RPI; r0 < BM; r0 += NW * RPI) {
-      const int row = r0 + lane / RP, pc = lane % RP;
+    for (int it = 0; it < BM / (NW * RPI); it++) {
+      const int row = (it * NW + wave) * RPI + lane / RP, pc = lane % RP;
       const int64_t m = m0 + row, n = col0 + pc * 8;
       const u32x4 v = *(const u32x4*)(t + row * BN + (pc ^ (row % RP)) * 8);
       if (m < a.M && n < ncols) *(u32x4*)(C + m * ldc + n) = v;

@@ -442,8 +442,8 @@ def main():
                     help="first run a plain float32 copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the Engram tables of every workload fit in one MI355X's HBM, so this "
-              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the Engram tables of every workload fit in one MI355X's HBM, and the "
+              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -254,6 +254,8 @@ def test_forward_within_tolerance(eg, name, n):
     (dict(batch=2, seqlen=2000), True),   # key channels 256-wide, then the value channels as a plain GEMM
     (dict(batch=1, seqlen=130, hidden=96, hc_mult=8), False),    # 8 branches; 24 of a wavefront's 64 lanes in the conv
     (dict(batch=2, seqlen=61, hidden=256, hc_mult=6, conv_kernel=3, conv_dilation=2), True),   # 6 branches
+    (dict(batch=2, seqlen=90, hidden=128, hc_mult=2, conv_kernel=1), True),    # one tap: no history
+    (dict(batch=1, seqlen=150, hidden=256, conv_kernel=8, conv_dilation=5), True),   # the largest conv
 ])
 def test_forward_paths_on_ragged_shapes(eg, over, fused):
     c = case("b4_t1024", **over)
@@ -312,6 +314,23 @@ def test_chunked_prefill_matches_single_prefill(eg):
     chunked = torch.cat(outs, dim=1)
     assert torch.equal(chunked, full)
     assert st.n_past.cpu().tolist() == [c.T] * c.B
+
+
+def test_chunks_with_the_largest_conv_match_single_prefill(eg):
+    """8 taps at dilation 5: the state's rings hold 36 positions, and chunks
+    shorter than the history (1, 3) read most of it from the rings."""
+    c = case("b4_t1024", batch=3, seqlen=140, hidden=256, conv_kernel=8, conv_dilation=5)
+    full = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    st = eg.State(c.cfg(), c.B)
+    outs, t0 = [], 0
+    for L in (1, 3, 40, 1, 95):
+        ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+        hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+        outs.append(eg.forward(c.cfg(c.B, L), c.params, ids, hid, state=st))
+        t0 += L
+    sync()
+    assert t0 == c.T
+    assert torch.equal(torch.cat(outs, dim=1), full)
 
 
 def test_long_chunks_match_single_prefill(eg):

@@ -247,6 +247,11 @@ def test_forward_within_tolerance(eg, name, n):
     assert err <= TOL[c.w.dtype], err
 
 
+# every count at its maximum: 8 orders (1..8) of 8 heads = 64 heads, 16 branches, 8 taps
+MAXIMAL = dict(orders=[1, 2, 3, 4, 5, 6, 7, 8], heads_per_order=8, head_dim=8, hidden=128, hc_mult=16,
+               conv_kernel=8, conv_dilation=8, prime_base=4001)
+
+
 @pytest.mark.parametrize("over,fused", [
     (dict(batch=2, seqlen=100, hidden=200, hc_mult=3), False),   # d % 128 != 0: stored projections + gate kernel
     (dict(batch=3, seqlen=77, hidden=256, hc_mult=2), True),     # fused GEMM with a ragged token count
@@ -256,6 +261,7 @@ def test_forward_within_tolerance(eg, name, n):
     (dict(batch=2, seqlen=61, hidden=256, hc_mult=6, conv_kernel=3, conv_dilation=2), True),   # 6 branches
     (dict(batch=2, seqlen=90, hidden=128, hc_mult=2, conv_kernel=1), True),    # one tap: no history
     (dict(batch=1, seqlen=150, hidden=256, conv_kernel=8, conv_dilation=5), True),   # the largest conv
+    (dict(MAXIMAL, batch=2, seqlen=40), True),   # 8 orders x 8 heads, 16 branches, 8 taps at dilation 8
 ])
 def test_forward_paths_on_ragged_shapes(eg, over, fused):
     c = case("b4_t1024", **over)
@@ -331,6 +337,26 @@ def test_chunks_with_the_largest_conv_match_single_prefill(eg):
     sync()
     assert t0 == c.T
     assert torch.equal(torch.cat(outs, dim=1), full)
+
+
+def test_chunks_with_every_count_at_its_maximum_match_single_prefill(eg):
+    """64 heads of orders up to 8 (a 7-token history from the token ring), 16
+    branches, 8 taps at dilation 8 (57-slot rings), in chunks of 1 to 30 tokens."""
+    c = case("b4_t1024", **dict(MAXIMAL, batch=2, seqlen=64))
+    full = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    st = eg.State(c.cfg(), c.B)
+    outs, t0 = [], 0
+    for L in (1, 2, 5, 1, 25, 30):
+        ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+        hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+        outs.append(eg.forward(c.cfg(c.B, L), c.params, ids, hid, state=st))
+        t0 += L
+    sync()
+    assert t0 == c.T
+    assert torch.equal(torch.cat(outs, dim=1), full)
+    pos = np.arange(c.B * c.T)
+    err = normwise(to_f64(full).reshape(c.B * c.T, c.w.hc_mult, c.w.hidden), c.y_at_many(pos))
+    assert err <= TOL["bf16"], err
 
 
 def test_long_chunks_match_single_prefill(eg):

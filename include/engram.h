@@ -70,7 +70,7 @@ typedef struct engram_config {
   int32_t seqlen;           /* T new tokens per sequence (T = 1 for a decode step) */
   int32_t vocab;            /* raw vocabulary size V; remap has V entries */
   int32_t n_orders;         /* number of n-gram orders, 1..ENGRAM_MAX_ORDERS */
-  int32_t orders[ENGRAM_MAX_ORDERS];   /* ascending n-gram orders, each >= 1 */
+  int32_t orders[ENGRAM_MAX_ORDERS];   /* ascending n-gram orders, each in 1..ENGRAM_MAX_ORDERS */
   int32_t heads_per_order;  /* hash heads per order; H = n_orders * heads_per_order <= ENGRAM_MAX_HEADS */
   int32_t head_dim;         /* embedding width of one head; E = H * head_dim, E % 8 == 0 */
   int32_t hidden;           /* d, hidden size of one branch; d % 8 == 0 */

@@ -262,6 +262,8 @@ MAXIMAL = dict(orders=[1, 2, 3, 4, 5, 6, 7, 8], heads_per_order=8, head_dim=8, h
     (dict(batch=2, seqlen=90, hidden=128, hc_mult=2, conv_kernel=1), True),    # one tap: no history
     (dict(batch=1, seqlen=150, hidden=256, conv_kernel=8, conv_dilation=5), True),   # the largest conv
     (dict(MAXIMAL, batch=2, seqlen=40), True),   # 8 orders x 8 heads, 16 branches, 8 taps at dilation 8
+    (dict(batch=5, seqlen=1), True),   # one token per sequence, no state: only the current tap
+    (dict(batch=3, seqlen=2), True),   # sequences shorter than the dilation (3)
 ])
 def test_forward_paths_on_ragged_shapes(eg, over, fused):
     c = case("b4_t1024", **over)

@@ -77,7 +77,8 @@ def _load():
         lib.orc_forward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P]
         lib.orc_forward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, ctypes.c_int64, P, P]
         lib.orc_backward.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, P, P, P, P, P, P, P, P]
-        lib.orc_backward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, rp, ctypes.c_int64, P, P, P]
+        lib.orc_backward_at.argtypes = [cp, P, ctypes.c_int32, P, rp, P, P, P, P, rp, rp, ctypes.c_int64, P, P, P,
+                                        P, P, P]
         for f in ("orc_shift", "orc_hash", "orc_gather", "orc_project", "orc_gate", "orc_conv", "orc_forward",
                   "orc_forward_at", "orc_backward", "orc_backward_at"):
             getattr(lib, f).restype = ctypes.c_int
@@ -277,10 +278,14 @@ class Oracle:
         return out
 
     def backward_at(self, ids, remap, table, w_kv, gamma_k, gamma_q, conv_w, hidden, dy, positions,
-                    table_keys=None, hidden_keys=None, dy_keys=None, want_de: bool = True):
-        """orc_backward_at: (d_hidden [P][hc][d], de [P][E] or None) at flat positions.
-        table, hidden and dy may be sparse (rows + ascending keys); hidden and dy
-        rows are keyed by flat position, [hc][d] each, in storage form."""
+                    table_keys=None, hidden_keys=None, dy_keys=None, want_de: bool = True, want_dkv: bool = False,
+                    want_dgamma: bool = False):
+        """orc_backward_at: (d_hidden [P][hc][d], de [P][E] or None) at flat positions;
+        with want_dkv also dkv [P][(hc+1)][d] (the keys' and value's gradient at
+        each position), with want_dgamma also (d_gamma_k, d_gamma_q) [hc][d], the
+        sums of the positions' terms.  table, hidden and dy may be sparse (rows +
+        ascending keys); hidden and dy rows are keyed by flat position, [hc][d]
+        each, in storage form."""
         c = self.cfg
         ids, rm = _c(ids, np.int32), _c(remap, np.int32)
         table = _c(table, self.store)
@@ -293,11 +298,19 @@ class Oracle:
         pos = _c(positions, np.int64)
         dh = np.empty((len(pos), c.hc_mult, c.hidden), np.float64)
         de = np.empty((len(pos), self.emb_dim), np.float64) if want_de else None
+        dkv = np.empty((len(pos), c.hc_mult + 1, c.hidden), np.float64) if want_dkv else None
+        dgk = np.zeros((c.hc_mult, c.hidden), np.float64) if want_dgamma else None
+        dgq = np.zeros((c.hc_mult, c.hidden), np.float64) if want_dgamma else None
         trows, hrows, yrows = self._rows(table, tk), self._rows(hidden, hk), self._rows(dy, yk)
         _ok(_load().orc_backward_at(ctypes.byref(c), _p(rm), len(rm), _p(ids), ctypes.byref(trows),
                                     *[_p(a) for a in args], ctypes.byref(hrows), ctypes.byref(yrows), len(pos),
-                                    _p(pos), _p(dh), _p(de)), "orc_backward_at")
-        return dh, de
+                                    _p(pos), _p(dh), _p(de), _p(dkv), _p(dgk), _p(dgq)), "orc_backward_at")
+        out = (dh, de)
+        if want_dkv:
+            out = out + (dkv,)
+        if want_dgamma:
+            out = out + (dgk, dgq)
+        return out
 
 
 def needed_positions(T: int, positions: np.ndarray, conv_kernel: int, dilation: int) -> np.ndarray:

@@ -552,11 +552,16 @@ out:
  * h's slice of de over the positions whose index is r).  A position reads e,
  * K, V, g and hidden at itself only, and dy at itself and D, 2D, ...,
  * (K-1)D positions later in its sequence: hidden and dy are row sources keyed
- * by flat position, one [hc][d] row each in the stored type. */
+ * by flat position, one [hc][d] row each in the stored type.
+ * Optional outputs (each NULL to skip): dkv [n_pos][(hc+1)*d], the gradient of
+ * the position's keys and value (the weight gradient is the sum over
+ * positions of dkv[p] (x) e[p]); d_gk and d_gq [hc][d], to which the
+ * positions' terms of the RMSNorm scales' gradients are added. */
 int orc_backward_at(const orc_config *c, const int32_t *remap, int32_t vocab, const int32_t *ids,
                     const orc_rows *table, const void *w_kv, const void *gamma_k, const void *gamma_q,
                     const void *conv_w, const orc_rows *hidden, const orc_rows *dy, int64_t n_pos,
-                    const int64_t *pos, double *d_hidden, double *de) {
+                    const int64_t *pos, double *d_hidden, double *de, double *dkv_out, double *d_gk,
+                    double *d_gq) {
   if (check(c)) return ORC_EINVAL;
   const int64_t T = c->seqlen, n = (int64_t)c->batch * T;
   const int H = n_heads(c), hc = c->hc_mult, K = c->conv_kernel, D = c->conv_dilation;
@@ -601,7 +606,8 @@ int orc_backward_at(const orc_config *c, const int32_t *remap, int32_t vocab, co
           dvg[(int64_t)h * d + ch] +=
               ld(conv_w, ((int64_t)h * d + ch) * K + j, c->dtype) * ld(dyr, (int64_t)h * d + ch, c->dtype);
     }
-    gate_backward_token(c, kv, q, gamma_k, gamma_q, dvg, g, s, dkv, d_hidden + i * hc * d, NULL, NULL);
+    gate_backward_token(c, kv, q, gamma_k, gamma_q, dvg, g, s, dkv, d_hidden + i * hc * d, d_gk, d_gq);
+    if (dkv_out) memcpy(dkv_out + i * O, dkv, sizeof(double) * O);
     if (de)
       for (int64_t k = 0; k < E; k++) {
         double acc = 0.0;

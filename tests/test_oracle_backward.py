@@ -117,8 +117,10 @@ def test_backward_zero_hidden_closed_form():
                                                          heads_per_order=2, prime_base=101))])
 def test_backward_at_matches_dense_backward(name, over):
     """orc_backward_at at every position (sparse rows, each keyed by flat
-    position) gives the dense backward's d hidden, and its de summed by
-    table row gives the dense d_table (both pinned above against autograd)."""
+    position) gives the dense backward's d hidden; its de summed by table row
+    gives the dense d_table, its dkv[p] (x) e[p] summed over positions the
+    dense d_w_kv, and its summed scale terms the dense d_gamma_k, d_gamma_q
+    (all pinned above against autograd)."""
     w = S.WORKLOADS[name].replace(**over)
     inp = S.Inputs(w)
     o = orc.Oracle.from_workload(w, inp, batch=w.batch, seqlen=w.seqlen)
@@ -134,10 +136,18 @@ def test_backward_at_matches_dense_backward(name, over):
     # positions in a shuffled order, hidden/dy as sparse rows keyed by position
     pos = np.random.default_rng(0).permutation(B * T)
     keys = np.arange(B * T, dtype=np.int64)
-    dh, de = o.backward_at(hidden=hidden, dy=dy, positions=pos, hidden_keys=keys, dy_keys=keys, **args)
+    dh, de, dkv, dgk, dgq = o.backward_at(hidden=hidden, dy=dy, positions=pos, hidden_keys=keys, dy_keys=keys,
+                                          want_dkv=True, want_dgamma=True, **args)
     ref_dh = dense["d_hidden"].reshape(B * T, w.hc_mult, w.hidden)[pos]
     assert np.abs(dh - ref_dh).max() <= 1e-12 * np.abs(ref_dh).max()
     idx = o.hash(inp.ids, remap=inp.remap).reshape(B * T, -1)[pos]
+    e = o.with_shape(1, len(pos)).gather(table, idx)
+    e64 = (e.astype(np.float32) if w.dtype == "f32" else S.bf16_bits_to_f32(e)).astype(np.float64)
+    dw = dkv.reshape(len(pos), -1).T @ e64
+    assert np.abs(dw - dense["d_w_kv"]).max() <= 1e-12 * np.abs(dense["d_w_kv"]).max()
+    for got, ref in ((dgk, dense["d_gamma_k"]), (dgq, dense["d_gamma_q"])):
+        assert np.abs(ref).max() > 0
+        assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
     off = np.concatenate([[0], np.cumsum(inp.primes)[:-1]])
     acc = np.zeros_like(dense["d_table"])
     H, Dh = idx.shape[1], w.head_dim
@@ -148,3 +158,35 @@ def test_backward_at_matches_dense_backward(name, over):
     with pytest.raises(orc.OracleError):
         o.backward_at(hidden=hidden[:5], dy=dy[:5], positions=pos[:1], hidden_keys=keys[:5], dy_keys=keys[:5],
                       **args)
+
+
+@pytest.mark.parametrize("name,over", [("tiny_fp32", dict(batch=2, seqlen=30, hc_mult=2)),
+                                       ("b4_t1024", dict(batch=3, seqlen=40, hidden=64, head_dim=8,
+                                                         heads_per_order=2, prime_base=101, hc_mult=2))])
+def test_sparse_dy_gradients_equal_dense_backward(name, over):
+    """The decomposition the large GPU backward tests rest on
+    (cases.sparse_dy_gradients): with dy zero except at a few positions, the
+    oracle's per-position gradients at P' = {p - jD} and the zero-tap forward's
+    Vg, summed over those positions, give the dense backward's gradients."""
+    from cases import Case, sparse_dy_gradients
+
+    c = Case(name, **over)
+    w = c.w
+    N, hc, d = c.B * c.T, w.hc_mult, w.hidden
+    rng = np.random.default_rng(3)
+    P = np.unique(np.concatenate([[0, c.T - 1, c.T, N - 1], rng.choice(N, 4, replace=False)]))
+    x = rng.standard_normal((len(P), hc, d)).astype(np.float32)
+    dy_val = x if w.dtype == "f32" else S.f32_to_bf16_bits(x)
+    dy64 = np.zeros((N, hc, d))
+    dy64[P] = x if w.dtype == "f32" else S.bf16_bits_to_f32(dy_val)
+    hid = c.inp.hidden().reshape(N, hc, d)
+    ref = sparse_dy_gradients(c, hid, P, dy_val, chunk=4)
+    gk, gq, cw = c.small
+    dense = c.orc.backward(ids=c.inp.ids, remap=c.inp.remap, table=c.inp.table(), w_kv=c.wkv, gamma_k=gk,
+                           gamma_q=gq, conv_w=cw, hidden=hid.reshape(c.B, c.T, hc, d),
+                           dy=dy64.reshape(c.B, c.T, hc, d))
+    for k, v in (("d_w_kv", "d_w_kv"), ("d_tables", "d_table"), ("d_gamma_k", "d_gamma_k"),
+                 ("d_gamma_q", "d_gamma_q"), ("d_conv_w", "d_conv_w"), ("d_hidden", "d_hidden")):
+        r = dense[v].reshape(ref[k].shape)
+        assert np.abs(r).max() > 0, k
+        assert np.abs(ref[k] - r).max() <= 1e-12 * np.abs(r).max(), k

@@ -415,6 +415,92 @@ def test_decode_matches_oracle(eg):
     assert normwise(got, ref) <= TOL[w.dtype]
 
 
+def _hash_with_history(c, ids_chunk, t0):
+    """The oracle's hash of a chunk that starts at position t0 of every
+    sequence, given as history the compressed ids of the max_order - 1
+    positions before it (pad before the sequence start)."""
+    W = c.w.max_order - 1
+    x = c.inp.remap[c.inp.ids]
+    hist = np.full((c.B, W), c.w.pad_id, dtype=np.int32)
+    for k in range(1, W + 1):
+        if t0 - k >= 0:
+            hist[:, W - k] = x[:, t0 - k]
+    L = ids_chunk.shape[1]
+    return c.orc.with_shape(c.B, L).hash(ids_chunk, remap=c.inp.remap, hist=hist)
+
+
+def test_decode_state_hash_and_gather_bit_exact(eg):
+    """Decode-shaped workload, the state path of the hash: the prompt's prefill
+    and each of the 512 single-token steps hash with the state (the tokens
+    before the step come from the state's token ring) and gather their rows
+    before the forward advances the state.  Every sequence's indices over all
+    528 positions equal the oracle's hash of the whole sequence, each step's
+    equal the oracle's hash of that step alone given the ids before it as
+    history, and the gathered rows equal the oracle's gather, bit for bit."""
+    from engram_synth.device import storage_numpy
+
+    c = case("decode_b256")
+    w = c.w
+    P, steps = w.decode_prompt, w.decode_steps
+    cfgp, cfg1 = c.cfg(c.B, P), c.cfg(c.B, 1)
+    ids, hid = c.dev["ids"], c.dev["hidden"]
+    st = eg.State(cfg1, c.B)
+    ws = eg.alloc_workspace(cfgp)
+    idx = [eg.engram_hash(cfgp, c.params, ids[:, :P].contiguous(), state=st)]
+    e = [eg.engram_gather(cfgp, c.params, idx[0])]
+    eg.forward(cfgp, c.params, ids[:, :P].contiguous(), hid[:, :P].contiguous(), state=st, workspace=ws)
+    steps_ids = ids[:, P:].t().contiguous()
+    steps_hid = hid[:, P:].transpose(0, 1).contiguous()
+    for s in range(steps):
+        i1 = eg.engram_hash(cfg1, c.params, steps_ids[s], state=st)
+        idx.append(i1)
+        e.append(eg.engram_gather(cfg1, c.params, i1))
+        eg.forward(cfg1, c.params, steps_ids[s], steps_hid[s], state=st, workspace=ws)
+    sync()
+    got = torch.cat([i.reshape(c.B, -1, c.w.n_heads) for i in idx], dim=1).cpu().numpy().astype(np.int64)
+    assert got.shape == c.idx.shape
+    assert np.array_equal(got, c.idx)
+    for s in (0, 1, 2, 3, 100, steps - 1):
+        t0 = P + s
+        ref = _hash_with_history(c, c.inp.ids[:, t0:t0 + 1], t0)
+        assert np.array_equal(idx[1 + s].cpu().numpy().reshape(c.B, 1, -1).astype(np.int64), ref), s
+    rows = np.concatenate([storage_numpy(x).reshape(c.B, -1, c.w.emb_dim) for x in e], axis=1)
+    rows = rows.reshape(c.B * c.T, -1)
+    for b0 in range(0, c.B, 64):     # every position, 64 sequences at a time
+        pos = np.arange(b0 * c.T, (b0 + 64) * c.T)
+        assert np.array_equal(rows[pos], c.e_at(pos)), b0
+
+
+def test_chunked_hash_and_gather_bit_exact(eg):
+    """Chunked prefill, the state path of the hash for chunks longer than one
+    token: each chunk's indices, hashed with the state before the forward
+    advances it, equal the oracle's hash of the chunk given the ids before it
+    as history, and its rows the oracle's gather; with orders up to 8 (a
+    7-token history from the ring) as well."""
+    from engram_synth.device import storage_numpy
+
+    for name, over, lens in (("b4_t1024", {}, (1, 2, 7, 100, 300, 614)),
+                             ("b4_t1024", dict(MAXIMAL, batch=2, seqlen=64), (1, 2, 5, 1, 25, 30))):
+        c = case(name, **over)
+        st = eg.State(c.cfg(), c.B)
+        t0 = 0
+        for L in lens:
+            ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+            hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+            cfg = c.cfg(c.B, L)
+            idx = eg.engram_hash(cfg, c.params, ids, state=st)
+            e = eg.engram_gather(cfg, c.params, idx)
+            eg.forward(cfg, c.params, ids, hid, state=st)
+            sync()
+            got = idx.cpu().numpy().astype(np.int64)
+            assert np.array_equal(got, _hash_with_history(c, c.inp.ids[:, t0:t0 + L], t0)), (name, t0, L)
+            assert np.array_equal(got, c.idx[:, t0:t0 + L]), (name, t0, L)
+            pos = (np.arange(c.B)[:, None] * c.T + np.arange(t0, t0 + L)[None, :]).ravel()
+            assert np.array_equal(storage_numpy(e).reshape(c.B * L, -1), c.e_at(pos)), (name, t0, L)
+            t0 += L
+        assert t0 == c.T
+
+
 def test_decode_state_copy_resumes(eg):
     """Checkpoint and resume of the decode state: after k steps the state is
     copied; the remaining steps run from the original and from the copy give
@@ -479,3 +565,59 @@ def ctypes_i64(v):
     import ctypes
 
     return ctypes.c_int64(int(v)).value
+
+
+# ------------------------------------------------------------------ kernel counts, debug build
+@pytest.mark.parametrize("name,over,T", [("b4_t1024", dict(batch=2, seqlen=100, hidden=200, hc_mult=3), None),
+                                         ("decode_b256", {}, 16), ("decode_b256", {}, 1), ("b4_t1024", {}, None)])
+def test_timed_forward_counts_the_kernels_it_names(eg, name, over, T):
+    """engram_forward_timed reports as many kernels as engram_forward_kernel_name
+    names, on every plan: stored projections, the fused projection, the decode
+    tail, and the split projection; with and without a state."""
+    c = case(name, **over)
+    T = c.T if T is None else T
+    cfg = c.cfg(c.B, T)
+    ids = c.dev["ids"][:, :T].contiguous()
+    hid = c.dev["hidden"][:, :T].contiguous()
+    plans = set()
+    for with_state in (False, True):
+        st = eg.State(cfg, c.B) if with_state else None
+        names = eg.kernel_names(cfg, with_state=with_state)
+        _, nk = eg.forward_timed(cfg, c.params, ids, hid, [], state=st)
+        sync()
+        assert nk == len(names), (names, nk)
+        plans.add(tuple(names))
+    assert len(plans) == 2
+
+
+def test_debug_build_rejects_out_of_range_ids(eg):
+    """The ENGRAM_DEBUG build checks the raw ids on the host: an id outside
+    [0, vocab) makes engram_hash and engram_forward return ENGRAM_EINVAL with
+    nothing enqueued (the release build hashes it as pad_id); valid ids give the
+    release build's indices."""
+    import ctypes
+
+    import hashed_gram_conditional_amd as m
+
+    dbg = m.load(debug=True)
+    c = case("tiny_fp32")
+    cfg = c.cfg()
+    out = torch.full((c.B, c.T, c.w.n_heads), -1, dtype=torch.int32, device="cuda")
+    args = lambda ids: (ctypes.byref(cfg), ctypes.byref(c.params._c), ctypes.c_void_p(ids.data_ptr()), None,
+                        ctypes.c_void_p(out.data_ptr()), None)
+    assert dbg.engram_hash(*args(c.dev["ids"])) == 0
+    sync()
+    assert torch.equal(out, eg.engram_hash(cfg, c.params, c.dev["ids"]))
+    for v in (-1, c.w.vocab):
+        bad = c.dev["ids"].clone()
+        bad[0, 7] = v
+        out.fill_(-1)
+        assert dbg.engram_hash(*args(bad)) == -1
+        sync()
+        assert bool((out == -1).all())
+        ws = eg.alloc_workspace(cfg)
+        y = torch.empty((c.B, c.T, c.w.hc_mult, c.w.hidden), dtype=torch.float32, device="cuda")
+        rc = dbg.engram_forward(ctypes.byref(cfg), ctypes.byref(c.params._c), ctypes.c_void_p(bad.data_ptr()),
+                                ctypes.c_void_p(c.dev["hidden"].data_ptr()), None, ctypes.c_void_p(y.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+        assert rc == -1

@@ -15,7 +15,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-from ._build import LIB_PATH, build, source_hash  # noqa: F401
+from ._build import DEBUG_LIB_PATH, LIB_PATH, build, source_hash  # noqa: F401
 
 MAX_ORDERS = 8
 MAX_HEADS = 64
@@ -111,46 +111,59 @@ class _State(ctypes.Structure):
 _lib = None
 
 
-def load():
-    """The loaded library; ImportError if it has not been built."""
+def load(debug: bool = False):
+    """The loaded library; ImportError if it has not been built.  debug=True:
+    the ENGRAM_DEBUG build (libengram_debug.so), whose calls also check on the
+    host that the raw token ids lie in [0, vocab)."""
     global _lib
+    if debug:
+        if "debug" not in _debug_lib:
+            _debug_lib["debug"] = _open(DEBUG_LIB_PATH)
+        return _debug_lib["debug"]
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
-        lib = ctypes.CDLL(LIB_PATH)
-        P, I = ctypes.c_void_p, ctypes.c_int
-        cfgp = ctypes.POINTER(EngramConfig)
-        prmp = ctypes.POINTER(_Params)
-        stp = ctypes.POINTER(_State)
-        lib.engram_workspace_size.argtypes = [cfgp]
-        lib.engram_workspace_size.restype = ctypes.c_size_t
-        lib.engram_state_bytes_per_sequence.argtypes = [cfgp]
-        lib.engram_state_bytes_per_sequence.restype = ctypes.c_size_t
-        lib.engram_hash.argtypes = [cfgp, prmp, P, stp, P, P]
-        lib.engram_hash_layers.argtypes = [cfgp, prmp, P, stp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P]
-        lib.engram_gather.argtypes = [cfgp, prmp, P, P, P]
-        lib.engram_gather_host.argtypes = [cfgp, P, P, P, ctypes.c_int32]
-        lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
-        lib.engram_gate_conv.argtypes = [cfgp, prmp, P, P, stp, P, P, P]
-        lib.engram_forward.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P]
-        lib.engram_forward_gathered.argtypes = [cfgp, prmp, P, P, P, stp, P, P, ctypes.c_size_t, P]
-        lib.engram_backward_workspace_size.argtypes = [cfgp]
-        lib.engram_backward_workspace_size.restype = ctypes.c_size_t
-        lib.engram_backward.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        lib.engram_forward_train.argtypes = [cfgp, prmp, P, P, P, P, ctypes.c_size_t, P]
-        lib.engram_backward_saved.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
-                                             ctypes.POINTER(ctypes.c_int32)]
-        lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
-        lib.engram_forward_kernel_name.restype = ctypes.c_char_p
-        lib.engram_status_string.argtypes = [I]
-        lib.engram_status_string.restype = ctypes.c_char_p
-        for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
-                  "engram_forward_gathered", "engram_backward", "engram_forward_train", "engram_backward_saved",
-                  "engram_forward_timed"):
-            getattr(lib, f).restype = I
-        _lib = lib
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+_debug_lib: dict = {}
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    cfgp = ctypes.POINTER(EngramConfig)
+    prmp = ctypes.POINTER(_Params)
+    stp = ctypes.POINTER(_State)
+    lib.engram_workspace_size.argtypes = [cfgp]
+    lib.engram_workspace_size.restype = ctypes.c_size_t
+    lib.engram_state_bytes_per_sequence.argtypes = [cfgp]
+    lib.engram_state_bytes_per_sequence.restype = ctypes.c_size_t
+    lib.engram_hash.argtypes = [cfgp, prmp, P, stp, P, P]
+    lib.engram_hash_layers.argtypes = [cfgp, prmp, P, stp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P]
+    lib.engram_gather.argtypes = [cfgp, prmp, P, P, P]
+    lib.engram_gather_host.argtypes = [cfgp, P, P, P, ctypes.c_int32]
+    lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
+    lib.engram_gate_conv.argtypes = [cfgp, prmp, P, P, stp, P, P, P]
+    lib.engram_forward.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P]
+    lib.engram_forward_gathered.argtypes = [cfgp, prmp, P, P, P, stp, P, P, ctypes.c_size_t, P]
+    lib.engram_backward_workspace_size.argtypes = [cfgp]
+    lib.engram_backward_workspace_size.restype = ctypes.c_size_t
+    lib.engram_backward.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.engram_forward_train.argtypes = [cfgp, prmp, P, P, P, P, ctypes.c_size_t, P]
+    lib.engram_backward_saved.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int32)]
+    lib.engram_forward_kernel_name.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
+    lib.engram_forward_kernel_name.restype = ctypes.c_char_p
+    lib.engram_status_string.argtypes = [I]
+    lib.engram_status_string.restype = ctypes.c_char_p
+    for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project",
+              "engram_gate_conv", "engram_forward", "engram_forward_gathered", "engram_backward",
+              "engram_forward_train", "engram_backward_saved", "engram_forward_timed"):
+        getattr(lib, f).restype = I
+    return lib
 
 
 # ------------------------------------------------------------------ marshalling
@@ -397,13 +410,30 @@ def forward(cfg: EngramConfig, p: Params, ids, hidden, state: Optional[State] = 
                                 _ptr(workspace), workspace.numel(), _stream(stream))
         _check("engram_forward", rc)
     else:
-        arr = (ctypes.c_void_p * len(events))(*events)
-        nk = ctypes.c_int32(0)
-        rc = lib.engram_forward_timed(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), st, _ptr(out),
-                                      _ptr(workspace), workspace.numel(), _stream(stream), arr, len(events),
-                                      ctypes.byref(nk))
-        _check("engram_forward_timed", rc)
+        forward_timed(cfg, p, ids, hidden, events, state=state, out=out, workspace=workspace, stream=stream)
     return out
+
+
+def forward_timed(cfg: EngramConfig, p: Params, ids, hidden, events, state: Optional[State] = None, out=None,
+                  workspace=None, stream=None):
+    """engram_forward_timed: forward with the i-th kernel bracketed by
+    events[2i], events[2i+1] (hipEvent_t handles).  Returns (out, number of
+    kernels launched)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult, cfg.hidden), dtype=_real_dtype(cfg),
+                          device=ids.device)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, ids.device)
+    st = None if state is None else ctypes.byref(state._c)
+    arr = (ctypes.c_void_p * max(len(events), 1))(*events)
+    nk = ctypes.c_int32(0)
+    rc = load().engram_forward_timed(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), st, _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream), arr, len(events),
+                                     ctypes.byref(nk))
+    _check("engram_forward_timed", rc)
+    return out, nk.value
 
 
 def forward_gathered(cfg: EngramConfig, p: Params, e, hidden, ids=None, state: Optional[State] = None, out=None,

@@ -3,6 +3,7 @@
 // order of kernel launches; and the host-memory gather for tables kept in
 // host memory.  Allocates nothing and keeps no mutable state.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -67,12 +68,36 @@ constexpr int kHostGatherBlocks = 32;
 
 int gather_grid_cap(const void* tables) {
   hipPointerAttribute_t at;
+  const hipError_t pending = hipPeekAtLastError();
   if (hipPointerGetAttributes(&at, tables) != hipSuccess) {
-    (void)hipGetLastError();   // not known to the runtime: treat as device memory, clear the error
+    // not known to the runtime: treat as device memory; clear the query's own
+    // error, but never one the caller had pending
+    if (pending == hipSuccess) (void)hipGetLastError();
     return 0;
   }
   return at.type == hipMemoryTypeHost ? kHostGatherBlocks : 0;
 }
+
+#ifdef ENGRAM_DEBUG
+// Debug builds only: the raw ids of a call must lie in [0, vocab) (release
+// builds hash an id outside that range as pad_id).  The ids are copied to the
+// host after the stream's earlier work, so the call waits.
+engram_status check_ids(const engram_config* c, const int32_t* ids, hipStream_t s) {
+  const int64_t n = (int64_t)c->batch * c->seqlen;
+  if (n == 0 || ids == nullptr) return ENGRAM_OK;
+  int32_t* h = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+  if (h == nullptr) return ENGRAM_EUNSUPPORTED;
+  engram_status rc = ENGRAM_OK;
+  if (hipStreamSynchronize(s) != hipSuccess || hipMemcpy(h, ids, (size_t)n * sizeof(int32_t), hipMemcpyDefault))
+    rc = ENGRAM_EHIP;
+  for (int64_t i = 0; rc == ENGRAM_OK && i < n; i++)
+    if (h[i] < 0 || h[i] >= c->vocab) rc = ENGRAM_EINVAL;
+  free(h);
+  return rc;
+}
+#else
+engram_status check_ids(const engram_config*, const int32_t*, hipStream_t) { return ENGRAM_OK; }
+#endif
 
 // the same, for calls that do not read the tables
 engram_status check_params_no_tables(const engram_config* c, const engram_params* p) {
@@ -262,6 +287,23 @@ bool decode_tail_path(const engram_config* c, bool with_state, bool gathered) {
   return with_state && !gathered && c->seqlen == 1 && p.tile && !p.split;
 }
 
+// The kernels a forward call launches, in order: *n of them from names[0]
+// (gathered: without the hash and gather).
+const char* const* forward_kernels(const engram_config* c, bool with_state, bool gathered, int* n) {
+  if (decode_tail_path(c, with_state, gathered)) {
+    *n = 3;
+    return kDecodeKernels;
+  }
+  const GatePlan plan = gate_plan(c);
+  const char* const* names = plan.split ? kSplitKernels : plan.tile ? kFusedKernels : kForwardKernels;
+  *n = with_state ? 5 : 4;   // advance_state is last
+  if (gathered) {
+    *n -= 1;
+    return names + 1;
+  }
+  return names;
+}
+
 GatherArgs gather_args(const engram_config* c, const engram_params* p, const int32_t* ids, const engram_state* st) {
   GatherArgs a;
   memset(&a, 0, sizeof a);
@@ -354,7 +396,8 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   const int64_t N = (int64_t)c->batch * c->seqlen;
   const GatePlan plan = gate_plan(c);
   const bool tail = decode_tail_path(c, st != nullptr, gathered);
-  const int nk = tail ? 3 : (st ? 5 : 4) - (gathered ? 1 : 0) + (plan.split ? 1 : 0);
+  int nk = 0;
+  (void)forward_kernels(c, st != nullptr, gathered, &nk);
   if (n_kernels) *n_kernels = N == 0 ? 0 : nk;
   if (N == 0) return ENGRAM_OK;
   if ((!gathered || st != nullptr) && ids == nullptr) return ENGRAM_EINVAL;
@@ -364,6 +407,7 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   const Workspace w = carve(c, ws);
   if (ws_bytes < w.bytes) return ENGRAM_ENOMEM;
   const bool bf16 = c->dtype == ENGRAM_BF16;
+  if ((!gathered || st != nullptr) && (rc = check_ids(c, ids, s))) return rc;
 
   HashConsts hc;
   make_hash_consts(c, &hc);
@@ -693,6 +737,7 @@ engram_status engram_hash(const engram_config* cfg, const engram_params* prm, co
   if ((rc = check_state(cfg, st))) return rc;
   if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
   if (ids == nullptr || idx_out == nullptr) return ENGRAM_EINVAL;
+  if ((rc = check_ids(cfg, ids, stream))) return rc;
   HashConsts hc;
   make_hash_consts(cfg, &hc);
   GatherArgs a;
@@ -717,6 +762,7 @@ engram_status engram_hash_layers(const engram_config* cfg, const engram_params* 
   if ((rc = check_state(cfg, st))) return rc;
   if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
   if (ids == nullptr || idx_out == nullptr) return ENGRAM_EINVAL;
+  if ((rc = check_ids(cfg, ids, stream))) return rc;
   HashConsts hc;
   make_hash_consts(cfg, &hc);
   LayerMults lm;
@@ -812,6 +858,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* prm
   engram_status rc = check_backward(cfg, prm, true, ids, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k,
                                     d_gamma_q, d_conv_w, workspace, workspace_bytes);
   if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
+  if ((rc = check_ids(cfg, ids, stream))) return rc;
   const BwdWorkspace w = carve_bwd(cfg, workspace);
   hipError_t e;
   if ((e = forward_quantities(cfg, prm, ids, hidden, w, stream))) return hip_status(e);
@@ -829,6 +876,7 @@ engram_status engram_forward_train(const engram_config* cfg, const engram_params
   if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(workspace, 256)) return ENGRAM_EINVAL;
   const BwdWorkspace w = carve_bwd(cfg, workspace);
   if (workspace_bytes < w.bytes) return ENGRAM_ENOMEM;
+  if ((rc = check_ids(cfg, ids, stream))) return rc;
   hipError_t e;
   if ((e = forward_quantities(cfg, prm, ids, hidden, w, stream))) return hip_status(e);
   const void* v = (const uint8_t*)w.kv + (int64_t)cfg->hc_mult * cfg->hidden * esize(cfg);
@@ -894,19 +942,28 @@ engram_status engram_gather_host(const engram_config* cfg, const void* tables, c
     copy(0, rows);
     return ENGRAM_OK;
   }
+  // Threads that cannot be started leave their share to this one; nothing
+  // thrown crosses the C interface.
   std::vector<std::thread> pool;
-  pool.reserve(nt);
-  for (int k = 0; k < nt; k++) pool.emplace_back(copy, rows * k / nt, rows * (k + 1) / nt);
+  int started = 0;
+  try {
+    pool.reserve(nt);
+    for (int k = 1; k < nt; k++) {
+      pool.emplace_back(copy, rows * k / nt, rows * (k + 1) / nt);
+      started = k;
+    }
+  } catch (...) {
+  }
+  copy(0, rows * 1 / nt);
+  if (started + 1 < nt) copy(rows * (started + 1) / nt, rows);
   for (auto& th : pool) th.join();
   return ENGRAM_OK;
 }
 
 const char* engram_forward_kernel_name(const engram_config* cfg, int32_t with_state, int32_t i) {
   if (validate(cfg) || i < 0) return nullptr;
-  if (decode_tail_path(cfg, with_state != 0, false)) return i < 3 ? kDecodeKernels[i] : nullptr;
-  const GatePlan plan = gate_plan(cfg);
-  const char* const* names = plan.split ? kSplitKernels : plan.tile ? kFusedKernels : kForwardKernels;
-  const int n = 5 - (with_state ? 0 : 1);   // advance_state is last
+  int n = 0;
+  const char* const* names = forward_kernels(cfg, with_state != 0, false, &n);
   return i < n ? names[i] : nullptr;
 }
 

@@ -44,6 +44,11 @@ def test_library_exports_every_declared_symbol(eg):
     lib = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert getattr(lib, n) is not None
+    # the debug build exports the same interface
+    out = subprocess.run(["nm", "-D", "--defined-only", eg.DEBUG_LIB_PATH], capture_output=True, text=True).stdout
+    exported_dbg = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert not [n for n in names if n not in exported_dbg]
+    assert eg.load(debug=True).engram_status_string(-1) == b"invalid configuration or argument"
 
 
 def good(eg, **over):
@@ -121,6 +126,17 @@ def test_status_strings_and_kernel_names(eg):
     assert lib.engram_status_string(-2) == b"workspace too small"
     assert eg.kernel_names(good(eg), with_state=True) == ["hash_gather", "project_gemm", "gate", "short_conv",
                                                          "advance_state"]
+    # every plan: stored projections, fused, split, decode tail
+    fused = dict(hidden=2560, hc_mult=4, orders=[2, 3], heads_per_order=8, head_dim=64,
+                 primes=list(range(1, 17)), multipliers=[3, 5, 7])
+    assert eg.kernel_names(good(eg, batch=16, seqlen=256, **fused)) == ["hash_gather", "project_gate_gemm",
+                                                                       "gate_finalize", "short_conv"]
+    assert eg.kernel_names(good(eg, batch=4, seqlen=1024, **dict(fused, hidden=1024))) == [
+        "hash_gather", "project_gate_gemm", "project_value_gemm", "short_conv"]
+    assert eg.kernel_names(good(eg, batch=256, seqlen=1, **fused), with_state=True) == [
+        "hash_gather", "project_gate_gemm", "decode_tail"]
+    assert eg.kernel_names(good(eg, batch=256, seqlen=1, **fused), with_state=False) == [
+        "hash_gather", "project_gate_gemm", "gate_finalize", "short_conv"]
 
 
 def test_forward_gathered_validates_on_the_host(eg):

@@ -27,7 +27,7 @@ STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too s
 # every entry point the header declares, in its order
 ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_hash_layers",
                 "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
-                "engram_forward_gathered", "engram_backward_workspace_size", "engram_backward",
+                "engram_forward_noalloc", "engram_forward_gathered", "engram_backward_workspace_size", "engram_backward",
                 "engram_forward_train", "engram_backward_saved",
                 "engram_forward_timed", "engram_forward_kernel_name", "engram_status_string"]
 
@@ -147,6 +147,7 @@ def _open(path):
     lib.engram_project.argtypes = [cfgp, prmp, P, P, P]
     lib.engram_gate_conv.argtypes = [cfgp, prmp, P, P, stp, P, P, P]
     lib.engram_forward.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P]
+    lib.engram_forward_noalloc.argtypes = [cfgp, prmp, P, P, stp, P, P]
     lib.engram_forward_gathered.argtypes = [cfgp, prmp, P, P, P, stp, P, P, ctypes.c_size_t, P]
     lib.engram_backward_workspace_size.argtypes = [cfgp]
     lib.engram_backward_workspace_size.restype = ctypes.c_size_t
@@ -160,7 +161,7 @@ def _open(path):
     lib.engram_status_string.argtypes = [I]
     lib.engram_status_string.restype = ctypes.c_char_p
     for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project",
-              "engram_gate_conv", "engram_forward", "engram_forward_gathered", "engram_backward",
+              "engram_gate_conv", "engram_forward", "engram_forward_noalloc", "engram_forward_gathered", "engram_backward",
               "engram_forward_train", "engram_backward_saved", "engram_forward_timed"):
         getattr(lib, f).restype = I
     return lib
@@ -434,6 +435,24 @@ def forward_timed(cfg: EngramConfig, p: Params, ids, hidden, events, state: Opti
                                      ctypes.byref(nk))
     _check("engram_forward_timed", rc)
     return out, nk.value
+
+
+NOALLOC_MAX_BYTES = 64 << 20   # ENGRAM_NOALLOC_MAX_BYTES
+
+
+def forward_noalloc(cfg: EngramConfig, p: Params, ids, hidden, state: Optional[State] = None, out=None, stream=None):
+    """engram_forward_noalloc: Engram.forward on the library's own device array
+    (no workspace; the library allocates nothing).  Returns out."""
+    import torch
+
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.seqlen, cfg.hc_mult, cfg.hidden), dtype=_real_dtype(cfg),
+                          device=ids.device)
+    st = None if state is None else ctypes.byref(state._c)
+    rc = load().engram_forward_noalloc(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), st, _ptr(out),
+                                       _stream(stream))
+    _check("engram_forward_noalloc", rc)
+    return out
 
 
 def forward_gathered(cfg: EngramConfig, p: Params, e, hidden, ids=None, state: Optional[State] = None, out=None,

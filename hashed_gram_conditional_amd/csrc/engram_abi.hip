@@ -1,18 +1,27 @@
 // Host side of the Engram C ABI (include/engram.h): argument validation, the
 // per-call hash constants, the workspace layout of engram_forward and the
 // order of kernel launches; and the host-memory gather for tables kept in
-// host memory.  Allocates nothing and keeps no mutable state.
+// host memory.  Allocates nothing; its only mutable state is the per-device
+// address of engram_forward_noalloc's device array.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <thread>
 #include <vector>
 
 #include "engram_internal.h"
 
 using namespace engram;
+
+// Device memory of engram_forward_noalloc, for callers that cannot allocate:
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never uses this name as an address: each device's copy is looked up
+// once with hipGetSymbolAddress and that address is what the kernels get.
+constexpr size_t kScratchBytes = ENGRAM_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -140,6 +149,30 @@ void make_hash_consts(const engram_config* c, HashConsts* hc) {
 }
 
 engram_status hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP; }
+
+// Address of the current device's copy of `scratch`, looked up on the first
+// call on that device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+engram_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ENGRAM_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return ENGRAM_EUNSUPPORTED;
+  try {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ENGRAM_EHIP;
+      g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+  } catch (...) {
+    return ENGRAM_EHIP;
+  }
+  return ENGRAM_OK;
+}
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -828,6 +861,16 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* prm,
                              size_t workspace_bytes, hipStream_t stream) {
   return forward_impl(cfg, prm, ids, false, nullptr, hidden, st, out, workspace, workspace_bytes, stream, nullptr, 0,
                       nullptr);
+}
+
+engram_status engram_forward_noalloc(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                     const void* hidden, engram_state* st, void* out, hipStream_t stream) {
+  engram_status rc = validate(cfg);
+  if (rc) return rc;
+  if (carve(cfg, nullptr).bytes > kScratchBytes) return ENGRAM_ENOMEM;
+  void* ws = nullptr;
+  if ((rc = device_scratch(&ws))) return rc;
+  return forward_impl(cfg, prm, ids, false, nullptr, hidden, st, out, ws, kScratchBytes, stream, nullptr, 0, nullptr);
 }
 
 engram_status engram_forward_gathered(const engram_config* cfg, const engram_params* prm, const int32_t* ids,

@@ -23,8 +23,10 @@
  *    tables, w_kv, gamma_k, gamma_q, conv_w, hidden, out, e and the value
  *    ring are 16-byte aligned (ENGRAM_EINVAL otherwise); ids, remap, gates and
  *    float32 gradient arrays need 4 bytes.
- *    The library allocates no memory and keeps no mutable global state; calls
- *    on different streams with disjoint outputs may run concurrently.
+ *    The library allocates no memory; calls on different streams with
+ *    disjoint outputs may run concurrently.  Its only global state is the
+ *    per-GPU device array of engram_forward_noalloc (and that array's address
+ *    on each GPU).
  *  - Calls validate their arguments on the host, enqueue kernels on `stream`
  *    (NULL = the null stream) and return without waiting.  A status other than
  *    ENGRAM_OK means nothing was enqueued.  Faults inside kernels surface as HIP
@@ -32,7 +34,10 @@
  *  - Layouts are dense row-major with the last index fastest.  N = batch*seqlen.
  *  - dtype selects the storage of tables, weights, gammas, conv taps, hidden,
  *    out and the value history: float32, or bfloat16 with float32 accumulation.
- *  - Token ids outside [0, vocab) are read as pad_id.
+ *  - Token ids outside [0, vocab) are read as pad_id.  The debug build of the
+ *    library (compiled with ENGRAM_DEBUG) checks the ids of every call that
+ *    reads them on the host first and returns ENGRAM_EINVAL for one outside
+ *    that range (the call then waits for the stream's earlier work).
  *  - No C++ exception crosses this interface.
  */
 #ifndef ENGRAM_H
@@ -180,6 +185,24 @@ engram_status engram_gate_conv(const engram_config *cfg, const engram_params *pr
 engram_status engram_forward(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
                              const void *hidden, engram_state *st, void *out, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Largest workspace (engram_workspace_size) engram_forward_noalloc serves. */
+#define ENGRAM_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+/* engram_forward without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the workspace is a device array inside the library, one
+ * copy of ENGRAM_NOALLOC_MAX_BYTES per GPU it runs on, held until the process
+ * ends.  It serves the GPU current on the calling thread (the stream's device).
+ * Configurations whose engram_workspace_size exceeds ENGRAM_NOALLOC_MAX_BYTES
+ * (e.g. 4096 tokens at hidden 1024 fit, 32768 tokens at hidden 2560 do not)
+ * return ENGRAM_ENOMEM before anything is enqueued.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  Every call
+ * on one GPU shares that array: calls that may overlap on one GPU (other
+ * streams, other threads) race, so the caller serialises them.  Otherwise as
+ * engram_forward, with the same results bit for bit. */
+engram_status engram_forward_noalloc(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                     const void *hidden, engram_state *st, void *out, hipStream_t stream);
 
 /* The module on rows gathered beforehand (walk-through 4.4, inference with the
  * tables in host memory: the hash depends only on the token ids, so the rows a

@@ -293,11 +293,30 @@ def bench_offload(args, w):
     p = eg.Params(remap=d["remap"], tables=d["tables"], w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
                   conv_w=d["conv_w"])
     t = d["tables"]
-    host = eg.alloc_mapped_host(t.numel() * t.element_size())
-    host.copy_from(t)
-    ph = eg.Params(remap=d["remap"], tables=host, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
-                   conv_w=d["conv_w"])
+    # pinned host memory mapped into the device serves both flows; where the
+    # host cannot pin the whole table (the 77 GB one), ordinary pageable memory
+    # serves the host+DMA flow alone (its reads are host threads' memcpy)
+    nbytes = t.numel() * t.element_size()
+    try:
+        if nbytes > 32 << 30:
+            raise MemoryError("table larger than the pinned host memory the box grants")
+        host = eg.alloc_mapped_host(nbytes)
+        host.copy_from(t)
+        host_tab = host
+    except MemoryError:
+        host = None
+        host_tab = torch.empty(t.shape, dtype=t.dtype)
+        rows = 1 << 22
+        for i in range(0, t.shape[0], rows):
+            host_tab[i:i + rows].copy_(t[i:i + rows])
+    ph = None if host is None else eg.Params(remap=d["remap"], tables=host, w_kv=d["w_kv"], gamma_k=d["gamma_k"],
+                                             gamma_q=d["gamma_q"], conv_w=d["conv_w"])
+    no_tables = eg.Params(remap=d["remap"], tables=None, w_kv=d["w_kv"], gamma_k=d["gamma_k"], gamma_q=d["gamma_q"],
+                          conv_w=d["conv_w"])
     N = w.batch * w.seqlen
+    free, total = torch.cuda.mem_get_info()
+    print(f"device memory free {free / 2**30:.1f} of {total / 2**30:.1f} GiB after the tables", file=sys.stderr,
+          flush=True)
     ws = eg.alloc_workspace(cfg)
     out = torch.empty((w.batch, w.seqlen, w.hc_mult, w.hidden), dtype=d["hidden"].dtype, device="cuda")
     idx = torch.empty((w.batch, w.seqlen, cfg.n_heads), dtype=torch.int32, device="cuda")
@@ -340,11 +359,11 @@ def bench_offload(args, w):
             ev_idx.record(side)
         ffn(layers)
         ev_idx.synchronize()                       # the host waits for the indices only
-        eg.engram_gather_host(cfg, host, idx_h, e_h)
+        eg.engram_gather_host(cfg, host_tab, idx_h, e_h)
         with torch.cuda.stream(side):
             e.copy_(e_h, non_blocking=True)
         main.wait_stream(side)
-        eg.forward_gathered(cfg, ph, e, d["hidden"], out=out, workspace=ws, stream=main)
+        eg.forward_gathered(cfg, no_tables, e, d["hidden"], out=out, workspace=ws, stream=main)
 
     def timed(fn, steps):
         for _ in range(3):
@@ -358,13 +377,14 @@ def bench_offload(args, w):
 
     steps = max(args.steps // 4, 10)
     # the two halves of the offloaded step alone: hash + gather from host vs from HBM
-    gather_host = timed(lambda: eg.engram_gather(cfg, ph, eg.engram_hash(cfg, ph, d["ids"], out=idx), out=e), steps)
+    gather_host = None if ph is None else timed(
+        lambda: eg.engram_gather(cfg, ph, eg.engram_hash(cfg, ph, d["ids"], out=idx), out=e), steps)
     gather_dev = timed(lambda: eg.engram_gather(cfg, p, eg.engram_hash(cfg, p, d["ids"], out=idx), out=e), steps)
     idx_h.copy_(idx)
-    eg.engram_gather_host(cfg, host, idx_h, e_h)   # first touch of the pinned buffers
+    eg.engram_gather_host(cfg, host_tab, idx_h, e_h)   # first touch of the pinned buffers
     t0 = time.perf_counter()
     for _ in range(steps):
-        eg.engram_gather_host(cfg, host, idx_h, e_h)
+        eg.engram_gather_host(cfg, host_tab, idx_h, e_h)
     gather_cpu = (time.perf_counter() - t0) / steps * 1e6
     h2d = timed(lambda: e.copy_(e_h, non_blocking=True), steps)
     rows_bytes = N * cfg.emb_dim * t.element_size()
@@ -376,19 +396,24 @@ def bench_offload(args, w):
         for _ in range(3):
             runs["ffn"].append(timed(lambda: ffn(layers), steps) if layers else 0.0)
             runs["r"].append(timed(lambda: resident(layers), steps))
-            runs["o"].append(timed(lambda: offloaded(layers), steps))
+            runs["o"].append(timed(lambda: offloaded(layers), steps) if ph is not None else None)
             runs["od"].append(timed(lambda: offloaded_dma(layers), steps))
-        ffn_us, r, o, od = (sorted(runs[k])[1] for k in ("ffn", "r", "o", "od"))
+        ffn_us, r, od = (sorted(runs[k])[1] for k in ("ffn", "r", "od"))
+        o = sorted(runs["o"])[1] if ph is not None else None
         rows.append({"ffn_layers": layers, "ffn_us": round(ffn_us, 1), "resident_us": round(r, 1),
-                     "zero_copy_us": round(o, 1), "zero_copy_loss": round(o / r - 1.0, 4),
+                     "zero_copy_us": None if o is None else round(o, 1),
+                     "zero_copy_loss": None if o is None else round(o / r - 1.0, 4),
                      "host_dma_us": round(od, 1), "host_dma_loss": round(od / r - 1.0, 4)})
     torch.cuda.synchronize()
-    host.free()
+    if host is not None:
+        host.free()
     res = {
         "mode": "offload", "workload": w.name, "tokens_per_step": N, "table_bytes": t.numel() * t.element_size(),
-        "host_tables": "pinned host memory, mapped, non-coherent (device may cache)",
-        "hash_gather_from_host_us": round(gather_host, 1), "hash_gather_from_hbm_us": round(gather_dev, 1),
-        "host_rows_GBps": round(rows_bytes / (gather_host * 1e-6) / 1e9, 1),
+        "host_tables": "pinned host memory, mapped, non-coherent (device may cache)" if host is not None else
+                       "pageable host memory (pinning the whole table failed): host+DMA flow only",
+        "hash_gather_from_host_us": None if gather_host is None else round(gather_host, 1),
+        "hash_gather_from_hbm_us": round(gather_dev, 1),
+        "host_rows_GBps": None if gather_host is None else round(rows_bytes / (gather_host * 1e-6) / 1e9, 1),
         "host_threads_gather_us": round(gather_cpu, 1), "rows_h2d_copy_us": round(h2d, 1),
         "steps": steps, "per_ffn_layers": rows,
     }
@@ -408,7 +433,7 @@ def bench_train(args, w):
 
     import engram_synth as S
     import hashed_gram_conditional_amd as eg
-    from engram_synth.device import device_inputs
+    from engram_synth.device import device_inputs, fill
 
     inp = S.Inputs(w)
     torch.cuda.set_device(0)
@@ -420,9 +445,18 @@ def bench_train(args, w):
     ws = eg.alloc_workspace(cfg)
     bws = eg.alloc_backward_workspace(cfg)
     out = torch.empty_like(d["hidden"])
-    dy = torch.randn(d["hidden"].shape, dtype=torch.float32, device="cuda").to(d["hidden"].dtype)
-    d_hidden, grads = eg.backward(cfg, p, d["ids"], d["hidden"], dy, workspace=bws)
+    dy = torch.empty_like(d["hidden"])
+    fill(dy, w.seed, *inp.recipe("dy"))
+    # the table gradient: dense float32 where it fits beside the tables, else
+    # row-sparse (the rows the step's hashes select, with their sums)
+    dense_bytes = w.table_rows * w.head_dim * 4
+    sparse = args.sparse or dense_bytes > 16 << 30
     stream = torch.cuda.current_stream()
+    if sparse:
+        d_hidden, grads, rows = eg.backward_sparse(cfg, p, d["ids"], d["hidden"], dy, workspace=bws)
+    else:
+        d_hidden, grads = eg.backward(cfg, p, d["ids"], d["hidden"], dy, workspace=bws)
+        rows = None
 
     def fwd():
         eg.forward(cfg, p, d["ids"], d["hidden"], out=out, workspace=ws, stream=stream)
@@ -431,10 +465,19 @@ def bench_train(args, w):
         eg.forward_train(cfg, p, d["ids"], d["hidden"], bws, out=out, stream=stream)
 
     def bwd_saved():
-        eg.backward_saved(cfg, p, d["hidden"], dy, bws, grads=grads, d_hidden=d_hidden, stream=stream)
+        if sparse:
+            eg.backward_saved_sparse(cfg, p, d["hidden"], dy, bws, grads=grads, rows=rows, d_hidden=d_hidden,
+                                     stream=stream)
+        else:
+            eg.backward_saved(cfg, p, d["hidden"], dy, bws, grads=grads, d_hidden=d_hidden, stream=stream)
 
     def bwd():
-        eg.backward(cfg, p, d["ids"], d["hidden"], dy, grads=grads, d_hidden=d_hidden, workspace=bws, stream=stream)
+        if sparse:
+            eg.backward_sparse(cfg, p, d["ids"], d["hidden"], dy, grads=grads, rows=rows, d_hidden=d_hidden,
+                               workspace=bws, stream=stream)
+        else:
+            eg.backward(cfg, p, d["ids"], d["hidden"], dy, grads=grads, d_hidden=d_hidden, workspace=bws,
+                        stream=stream)
 
     def train():
         fwd_train()
@@ -464,6 +507,8 @@ def bench_train(args, w):
         "inference_forward_ms": round(fwd_ms, 4), "backward_recompute_ms": round(bwd_ms, 4),
         "steps": args.steps, "warmup": args.warmup,
         "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "tokens_per_step": N},
+        "table_gradient": "row-sparse (rows used: %d of %d)" % (int(rows["n_rows"].item()), w.table_rows)
+                          if sparse else "dense float32",
         "backward_gemm_flops": flops, "backward_gemm_TFLOPs_over_backward_time": round(tflops, 1),
         "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if w.dtype == "bf16" else None,
         "workspace_bytes": {"forward": ws.numel(), "backward": bws.numel()},
@@ -519,6 +564,8 @@ def main():
                     help="host build of the compressed-id table from a synthetic vocabulary of the workload's size")
     ap.add_argument("--train", action="store_true",
                     help="forward + backward (gradients of the tables and weights) per step")
+    ap.add_argument("--sparse", action="store_true",
+                    help="with --train: the table gradient row-sparse (automatic when a dense one exceeds 16 GiB)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain float32 copy of this many MiB (counter calibration)")
     args = ap.parse_args()

@@ -28,6 +28,7 @@ STATUS = {0: "ok", -1: "invalid configuration or argument", -2: "workspace too s
 ENTRY_POINTS = ["engram_workspace_size", "engram_state_bytes_per_sequence", "engram_hash", "engram_hash_layers",
                 "engram_gather", "engram_gather_host", "engram_project", "engram_gate_conv", "engram_forward",
                 "engram_forward_noalloc", "engram_forward_gathered", "engram_backward_workspace_size", "engram_backward",
+                "engram_backward_sparse", "engram_backward_saved_sparse",
                 "engram_forward_train", "engram_backward_saved",
                 "engram_forward_timed", "engram_forward_kernel_name", "engram_status_string"]
 
@@ -153,6 +154,8 @@ def _open(path):
     lib.engram_backward_workspace_size.restype = ctypes.c_size_t
     lib.engram_backward.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.engram_forward_train.argtypes = [cfgp, prmp, P, P, P, P, ctypes.c_size_t, P]
+    lib.engram_backward_sparse.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.engram_backward_saved_sparse.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.engram_backward_saved.argtypes = [cfgp, prmp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.engram_forward_timed.argtypes = [cfgp, prmp, P, P, stp, P, P, ctypes.c_size_t, P, P, ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_int32)]
@@ -162,7 +165,8 @@ def _open(path):
     lib.engram_status_string.restype = ctypes.c_char_p
     for f in ("engram_hash", "engram_hash_layers", "engram_gather", "engram_gather_host", "engram_project",
               "engram_gate_conv", "engram_forward", "engram_forward_noalloc", "engram_forward_gathered", "engram_backward",
-              "engram_forward_train", "engram_backward_saved", "engram_forward_timed"):
+              "engram_forward_train", "engram_backward_saved", "engram_forward_timed", "engram_backward_sparse",
+              "engram_backward_saved_sparse"):
         getattr(lib, f).restype = I
     return lib
 
@@ -485,13 +489,15 @@ def alloc_backward_workspace(cfg: EngramConfig, device="cuda"):
     return torch.empty((max(backward_workspace_size(cfg), 256),), dtype=torch.uint8, device=device)
 
 
-def _zero_grads(cfg: EngramConfig, dev):
+def _zero_grads(cfg: EngramConfig, dev, tables: bool = True):
     import torch
 
     E, d, hc = cfg.emb_dim, cfg.hidden, cfg.hc_mult
     rows = sum(int(cfg.primes[h]) for h in range(cfg.n_heads))
     shapes = {"d_tables": (rows, cfg.head_dim), "d_w_kv": ((hc + 1) * d, E), "d_gamma_k": (hc, d),
               "d_gamma_q": (hc, d), "d_conv_w": (hc, d, cfg.conv_kernel)}
+    if not tables:
+        del shapes["d_tables"]
     return {k: torch.zeros(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
 
 
@@ -513,6 +519,62 @@ def backward(cfg: EngramConfig, p: Params, ids, hidden, dy, grads=None, d_hidden
                                 workspace.numel(), _stream(stream))
     _check("engram_backward", rc)
     return d_hidden, grads
+
+
+SPARSE_GRAD_NAMES = ("d_w_kv", "d_gamma_k", "d_gamma_q", "d_conv_w")
+
+
+def _sparse_outputs(cfg: EngramConfig, dev):
+    import torch
+
+    n = cfg.batch * cfg.seqlen * cfg.n_heads
+    return {"row_index": torch.empty((n,), dtype=torch.int64, device=dev),
+            "d_rows": torch.empty((n, cfg.head_dim), dtype=torch.float32, device=dev),
+            "n_rows": torch.empty((1,), dtype=torch.int64, device=dev)}
+
+
+def backward_sparse(cfg: EngramConfig, p: Params, ids, hidden, dy, grads=None, rows=None, d_hidden=None,
+                    workspace=None, stream=None):
+    """Gradients with the table gradient row-sparse: returns (d_hidden, grads,
+    rows), rows = {"row_index", "d_rows", "n_rows"} (the first n_rows entries
+    valid); grads holds the dense parameter gradients (added to)."""
+    import torch
+
+    dev = ids.device
+    if grads is None:
+        grads = {k: v for k, v in _zero_grads(cfg, dev, tables=False).items()}
+    if rows is None:
+        rows = _sparse_outputs(cfg, dev)
+    if d_hidden is None:
+        d_hidden = torch.empty_like(hidden)
+    if workspace is None:
+        workspace = alloc_backward_workspace(cfg, dev)
+    rc = load().engram_backward_sparse(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(ids), _ptr(hidden), _ptr(dy),
+                                       _ptr(d_hidden), _ptr(rows["row_index"]), _ptr(rows["d_rows"]),
+                                       _ptr(rows["n_rows"]), *[_ptr(grads[k]) for k in SPARSE_GRAD_NAMES],
+                                       _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("engram_backward_sparse", rc)
+    return d_hidden, grads, rows
+
+
+def backward_saved_sparse(cfg: EngramConfig, p: Params, hidden, dy, workspace, grads=None, rows=None, d_hidden=None,
+                          stream=None):
+    """backward_sparse on the quantities forward_train kept in `workspace`."""
+    import torch
+
+    dev = hidden.device
+    if grads is None:
+        grads = {k: v for k, v in _zero_grads(cfg, dev, tables=False).items()}
+    if rows is None:
+        rows = _sparse_outputs(cfg, dev)
+    if d_hidden is None:
+        d_hidden = torch.empty_like(hidden)
+    rc = load().engram_backward_saved_sparse(ctypes.byref(cfg), ctypes.byref(p._c), _ptr(hidden), _ptr(dy),
+                                             _ptr(d_hidden), _ptr(rows["row_index"]), _ptr(rows["d_rows"]),
+                                             _ptr(rows["n_rows"]), *[_ptr(grads[k]) for k in SPARSE_GRAD_NAMES],
+                                             _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("engram_backward_saved_sparse", rc)
+    return d_hidden, grads, rows
 
 
 def forward_train(cfg: EngramConfig, p: Params, ids, hidden, workspace, out=None, stream=None):

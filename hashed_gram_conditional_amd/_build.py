@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libengram.so")
 DEBUG_LIB_PATH = os.path.join(PKG, "libengram_debug.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
-SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gemm_tn.hip", "gate_conv.hip", "backward.hip"]
+SOURCES = ["engram_abi.hip", "hash_gather.hip", "gemm.hip", "gemm_tn.hip", "gate_conv.hip", "backward.hip",
+           "sparse_grad.hip"]
 HEADERS = ["engram_internal.h", "gemm_common.h", os.path.join("..", "..", "include", "engram.h")]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC", "-std=c++20", "-Wall",
@@ -27,7 +28,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-fPIC
 
 
 # the sources the forward kernels are built from (the gradients' kernels are not among them)
-FORWARD_SOURCES = [f for f in SOURCES if f not in ("backward.hip", "gemm_tn.hip")]
+FORWARD_SOURCES = [f for f in SOURCES if f not in ("backward.hip", "gemm_tn.hip", "sparse_grad.hip")]
 
 
 def source_hash() -> str:

@@ -242,6 +242,10 @@ struct BwdWorkspace {
   float* wpart;     // [S][(hc+1)d][E] when S > 1: the splits' products
   float* gpart;     // [gate_bwd_rows(N)][hc][d]: per-block sums for the gammas' gradients
   float* cpart;     // [conv_bwd_rows][hc][d][K]: per-block sums for the taps' gradients
+  uint32_t* bits;   // row-sparse table gradient: [sparse_bitmap_words] bitmap of the rows used
+  uint32_t* count;  // [sparse_groups] set bits per group of the bitmap
+  uint32_t* first;  // [sparse_groups] first rank of each group
+  uint32_t* rank;   // [N][H] rank of each pair's row
   int64_t Np;       // S chunks of Ks tokens (multiples of 64), zero past N
   int64_t Ks;
   int S;
@@ -301,6 +305,12 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.gpart = (float*)take((size_t)gate_bwd_rows(N) * c->hc_mult * c->hidden * sizeof(float));
   w.cpart = (float*)take((size_t)conv_bwd_rows(c->batch, c->seqlen) * c->hc_mult * c->hidden * c->conv_kernel *
                          sizeof(float));
+  int64_t rows = 0;
+  for (int h = 0; h < n_heads(c); h++) rows += c->primes[h];
+  w.bits = (uint32_t*)take((size_t)sparse_bitmap_words(rows) * sizeof(uint32_t));
+  w.count = (uint32_t*)take((size_t)sparse_groups(rows) * sizeof(uint32_t));
+  w.first = (uint32_t*)take((size_t)sparse_groups(rows) * sizeof(uint32_t));
+  w.rank = (uint32_t*)take((size_t)N * n_heads(c) * sizeof(uint32_t));
   w.bytes = off;
   return w;
 }
@@ -561,23 +571,38 @@ engram_status forward_impl(const engram_config* c, const engram_params* p, const
   return ENGRAM_OK;
 }
 
+// The table gradient in row-sparse form: the rows used, ascending, their
+// gradients and their count (all device memory, written).
+struct SparseOut {
+  int64_t* row_index;
+  float* d_rows;
+  int64_t* n_rows;
+};
+
 // Checks shared by the backward entry points (ids only when the forward
 // quantities are recomputed).
 engram_status check_backward(const engram_config* cfg, const engram_params* prm, bool need_ids, const int32_t* ids,
                              const void* hidden, const void* dy, void* d_hidden, float* d_tables, float* d_w_kv,
                              float* d_gamma_k, float* d_gamma_q, float* d_conv_w, void* workspace,
-                             size_t workspace_bytes) {
+                             size_t workspace_bytes, const SparseOut* sp = nullptr) {
   engram_status rc = validate(cfg);
   if (rc) return rc;
   if ((rc = need_ids ? check_params(cfg, prm) : check_params_no_tables(cfg, prm))) return rc;
   if ((int64_t)cfg->batch * cfg->seqlen == 0) return ENGRAM_OK;
+  if (sp) {   // ranks are 32-bit
+    if ((int64_t)cfg->batch * cfg->seqlen * n_heads(cfg) >= INT32_MAX) return ENGRAM_EUNSUPPORTED;
+    if (sp->row_index == nullptr || sp->d_rows == nullptr || sp->n_rows == nullptr || !aligned(sp->row_index, 8) ||
+        !aligned(sp->d_rows, 4) || !aligned(sp->n_rows, 8))
+      return ENGRAM_EINVAL;
+  } else if (d_tables == nullptr || !aligned(d_tables, 4)) {
+    return ENGRAM_EINVAL;
+  }
   if ((need_ids && ids == nullptr) || hidden == nullptr || dy == nullptr || d_hidden == nullptr ||
-      d_tables == nullptr || d_w_kv == nullptr || d_gamma_k == nullptr || d_gamma_q == nullptr ||
-      d_conv_w == nullptr || workspace == nullptr)
+      d_w_kv == nullptr || d_gamma_k == nullptr || d_gamma_q == nullptr || d_conv_w == nullptr ||
+      workspace == nullptr)
     return ENGRAM_EINVAL;
   if (!aligned(hidden, 16) || !aligned(dy, 16) || !aligned(d_hidden, 16) || !aligned(workspace, 256) ||
-      !aligned(d_tables, 4) || !aligned(d_w_kv, 4) || !aligned(d_gamma_k, 4) || !aligned(d_gamma_q, 4) ||
-      !aligned(d_conv_w, 4))
+      !aligned(d_w_kv, 4) || !aligned(d_gamma_k, 4) || !aligned(d_gamma_q, 4) || !aligned(d_conv_w, 4))
     return ENGRAM_EINVAL;
   if (workspace_bytes < carve_bwd(cfg, nullptr).bytes) return ENGRAM_ENOMEM;
   return ENGRAM_OK;
@@ -643,7 +668,7 @@ hipError_t forward_quantities(const engram_config* cfg, const engram_params* prm
 // Gradients from the forward quantities in the workspace.
 engram_status gradients(const engram_config* cfg, const engram_params* prm, const void* hidden, const void* dy,
                         void* d_hidden, float* d_tables, float* d_w_kv, float* d_gamma_k, float* d_gamma_q,
-                        float* d_conv_w, const BwdWorkspace& w, hipStream_t stream) {
+                        float* d_conv_w, const BwdWorkspace& w, hipStream_t stream, const SparseOut* sp = nullptr) {
   const int64_t N = (int64_t)cfg->batch * cfg->seqlen;
   const bool bf16 = cfg->dtype == ENGRAM_BF16;
   const int64_t E = emb_dim(cfg), O = (int64_t)(cfg->hc_mult + 1) * cfg->hidden;
@@ -712,7 +737,26 @@ engram_status gradients(const engram_config* cfg, const engram_params* prm, cons
   g1.K = (int32_t)O;
   g1.accumulate = 0;
   if ((e = bf16 ? launch_gemm_bf16_f32out(g1, stream) : launch_gemm_f32(g1, stream))) return hip_status(e);
-  if ((e = launch_scatter_add(hc, w.idx, w.de, d_tables, N, cfg->head_dim, stream))) return hip_status(e);
+  if (sp) {
+    SparseRowsArgs sa;
+    sa.hc = hc;
+    sa.idx = w.idx;
+    sa.de = w.de;
+    sa.n_tok = N;
+    sa.head_dim = cfg->head_dim;
+    sa.table_rows = 0;
+    for (int h = 0; h < hc.n_heads; h++) sa.table_rows += cfg->primes[h];
+    sa.bits = w.bits;
+    sa.count = w.count;
+    sa.first = w.first;
+    sa.pair_rank = w.rank;
+    sa.row_index = sp->row_index;
+    sa.d_rows = sp->d_rows;
+    sa.n_rows = sp->n_rows;
+    if ((e = launch_sparse_rows(sa, stream))) return hip_status(e);
+  } else if ((e = launch_scatter_add(hc, w.idx, w.de, d_tables, N, cfg->head_dim, stream))) {
+    return hip_status(e);
+  }
   // dW += dKV^T e
   // (in S split-K chunks of the token axis when the output has too few tiles
   // to fill the chip; the chunks' products are then added in chunk order)
@@ -937,6 +981,34 @@ engram_status engram_backward_saved(const engram_config* cfg, const engram_param
   if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
   return gradients(cfg, prm, hidden, dy, d_hidden, d_tables, d_w_kv, d_gamma_k, d_gamma_q, d_conv_w,
                    carve_bwd(cfg, workspace), stream);
+}
+
+engram_status engram_backward_sparse(const engram_config* cfg, const engram_params* prm, const int32_t* ids,
+                                     const void* hidden, const void* dy, void* d_hidden, int64_t* row_index,
+                                     float* d_rows, int64_t* n_rows, float* d_w_kv, float* d_gamma_k, float* d_gamma_q,
+                                     float* d_conv_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const SparseOut sp{row_index, d_rows, n_rows};
+  engram_status rc = check_backward(cfg, prm, true, ids, hidden, dy, d_hidden, nullptr, d_w_kv, d_gamma_k,
+                                    d_gamma_q, d_conv_w, workspace, workspace_bytes, &sp);
+  if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
+  if ((rc = check_ids(cfg, ids, stream))) return rc;
+  const BwdWorkspace w = carve_bwd(cfg, workspace);
+  hipError_t e;
+  if ((e = forward_quantities(cfg, prm, ids, hidden, w, stream))) return hip_status(e);
+  return gradients(cfg, prm, hidden, dy, d_hidden, nullptr, d_w_kv, d_gamma_k, d_gamma_q, d_conv_w, w, stream, &sp);
+}
+
+engram_status engram_backward_saved_sparse(const engram_config* cfg, const engram_params* prm, const void* hidden,
+                                           const void* dy, void* d_hidden, int64_t* row_index, float* d_rows,
+                                           int64_t* n_rows, float* d_w_kv, float* d_gamma_k, float* d_gamma_q,
+                                           float* d_conv_w, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  const SparseOut sp{row_index, d_rows, n_rows};
+  engram_status rc = check_backward(cfg, prm, false, nullptr, hidden, dy, d_hidden, nullptr, d_w_kv, d_gamma_k,
+                                    d_gamma_q, d_conv_w, workspace, workspace_bytes, &sp);
+  if (rc || (int64_t)cfg->batch * cfg->seqlen == 0) return rc;
+  return gradients(cfg, prm, hidden, dy, d_hidden, nullptr, d_w_kv, d_gamma_k, d_gamma_q, d_conv_w,
+                   carve_bwd(cfg, workspace), stream, &sp);
 }
 
 engram_status engram_gather_host(const engram_config* cfg, const void* tables, const int32_t* idx, void* e_out,

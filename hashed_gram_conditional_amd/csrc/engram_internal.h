@@ -288,6 +288,27 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t co
 hipError_t launch_scatter_add(const HashConsts& hc, const int32_t* idx, const float* de, float* d_tables,
                               int64_t n_tok, int32_t head_dim, hipStream_t s);
 
+// Row-sparse table gradient: the rows the pairs select, once each and
+// ascending, with the sums of de over the pairs that selected them.
+struct SparseRowsArgs {
+  HashConsts hc;
+  const int32_t* idx;    // [N][H]
+  const float* de;       // [N][H * head_dim]
+  int64_t n_tok;
+  int32_t head_dim;
+  int64_t table_rows;    // sum of the primes
+  uint32_t* bits;        // [sparse_bitmap_words] scratch
+  uint32_t* count;       // [sparse_groups] scratch
+  uint32_t* first;       // [sparse_groups] scratch
+  uint32_t* pair_rank;   // [N * H] scratch
+  int64_t* row_index;    // [N * H] out: the rows, ascending (the first *n_rows valid)
+  float* d_rows;         // [N * H][head_dim] out: their gradients
+  int64_t* n_rows;       // [1] out
+};
+int64_t sparse_bitmap_words(int64_t table_rows);
+int64_t sparse_groups(int64_t table_rows);
+hipError_t launch_sparse_rows(const SparseRowsArgs& a, hipStream_t s);
+
 struct AdvanceArgs {
   const int32_t* ids;     // [B][T] raw
   const int32_t* remap;   // or null

@@ -265,6 +265,35 @@ engram_status engram_backward_saved(const engram_config *cfg, const engram_param
                                     float *d_gamma_k, float *d_gamma_q, float *d_conv_w, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* engram_backward with the table gradient in row-sparse form, for tables too
+ * large for a dense float32 gradient (the walk-through, 4.4, trains tables of
+ * up to 100B parameters; a step reads at most N * H of their rows): the rows
+ * the step's hashes select, each once, ascending, with the sum of the
+ * gradient over the (token, head) pairs that selected them.
+ *   row_index [N*H] int64, 8-byte aligned: row_index[0 .. *n_rows) are the
+ *     stacked-table rows (written);
+ *   d_rows [N*H][head_dim] float32: d_rows[i] is row_index[i]'s gradient
+ *     (written, not added to: the rows differ from step to step);
+ *   n_rows [1] int64 (device memory, written; read it after the stream's work).
+ * The other gradients as engram_backward (added to, or written for d_hidden);
+ * the row sums use float32 atomics, so their last bits may differ between
+ * runs.  ENGRAM_EUNSUPPORTED when N*H >= 2^31.  Workspace: the same
+ * engram_backward_workspace_size.  Errors as engram_backward. */
+engram_status engram_backward_sparse(const engram_config *cfg, const engram_params *prm, const int32_t *ids,
+                                     const void *hidden, const void *dy, void *d_hidden, int64_t *row_index,
+                                     float *d_rows, int64_t *n_rows, float *d_w_kv, float *d_gamma_k,
+                                     float *d_gamma_q, float *d_conv_w, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* engram_backward_saved with the table gradient in row-sparse form (as
+ * engram_backward_sparse), on the forward quantities engram_forward_train
+ * left in `workspace`. */
+engram_status engram_backward_saved_sparse(const engram_config *cfg, const engram_params *prm, const void *hidden,
+                                           const void *dy, void *d_hidden, int64_t *row_index, float *d_rows,
+                                           int64_t *n_rows, float *d_w_kv, float *d_gamma_k, float *d_gamma_q,
+                                           float *d_conv_w, void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
 /* Same as engram_forward, additionally recording events[2i] / events[2i+1]
  * (caller-created hipEvent_t) on `stream` around the i-th kernel it launches,
  * for i < n_events/2.  Returns the number of kernels in *n_kernels (nullable).

@@ -8,7 +8,8 @@
 // all heads into e_t).
 //
 // Layout of the work: one 256-thread workgroup takes 16 consecutive tokens
-// (flattened over batch and time).  It stages the compressed ids of those
+// (flattened over batch and time; fewer when the call has too few tokens to
+// give every CU two workgroups).  It stages the compressed ids of those
 // tokens plus the max_order-1 tokens before them in LDS (one remap lookup per
 // token instead of one per (token, head, offset)), hashes every (token, head)
 // pair into a global table row kept in LDS, then copies the rows to e_t in
@@ -27,7 +28,7 @@ namespace engram {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokens = 16;
+constexpr int kTokens = 16;       // tokens per workgroup (at most)
 constexpr int kUnroll = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte piece
@@ -103,19 +104,22 @@ __device__ __forceinline__ uint32_t hash_one(const HashConsts& hc, const GatherA
   return floored_mod(mix, hc.prime[h], hc.magic[h], hc.wrap[h]);
 }
 
-template <typename Chunk>
+// TOK tokens per workgroup: 16 on large calls; fewer on small ones (decode
+// steps), so that the work spreads over more compute units
+template <typename Chunk, int TOK>
 __global__ void __launch_bounds__(kThreads) k_hash_gather(HashConsts hc, GatherArgs a, int compute_hash) {
-  __shared__ int32_t s_x[kTokens + ENGRAM_MAX_ORDERS];
-  __shared__ int32_t s_hist[kTokens * ENGRAM_MAX_ORDERS];
-  __shared__ int64_t s_row[kTokens * ENGRAM_MAX_HEADS];
+  static_assert(TOK <= kTokens, "staging sized for kTokens");
+  __shared__ int32_t s_x[TOK + ENGRAM_MAX_ORDERS];
+  __shared__ int32_t s_hist[TOK * ENGRAM_MAX_ORDERS];
+  __shared__ int64_t s_row[TOK * ENGRAM_MAX_HEADS];
 
   const int64_t N = (int64_t)a.batch * a.seqlen;
   const int H = hc.n_heads;
   const int tid = threadIdx.x;
-  const int64_t n_tiles = (N + kTokens - 1) / kTokens;
+  const int64_t n_tiles = (N + TOK - 1) / TOK;
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t n0 = tile * kTokens;
-    const int ntok = (int)min((int64_t)kTokens, N - n0);
+    const int64_t n0 = tile * TOK;
+    const int ntok = (int)min((int64_t)TOK, N - n0);
 
     if (compute_hash) {
       if (a.past_out)   // n_past before this call, for kernels that advance the state later
@@ -208,21 +212,36 @@ hipError_t launch_hash_layers(const HashConsts& hc, const LayerMults& lm, const 
   return hipGetLastError();
 }
 
-hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
-                              int max_blocks) {
+template <int TOK>
+hipError_t hash_gather_tok(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
+                           int max_blocks) {
   const int64_t N = (int64_t)a.batch * a.seqlen;
-  if (N == 0) return hipSuccess;
-  int64_t tiles = (N + kTokens - 1) / kTokens;
+  int64_t tiles = (N + TOK - 1) / TOK;
   if (max_blocks > 0 && tiles > max_blocks) tiles = max_blocks;
   const unsigned blocks = (unsigned)tiles;
   const int ch = compute_hash ? 1 : 0;
   if (a.row_bytes % 16 == 0)
-    k_hash_gather<u32x4><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+    k_hash_gather<u32x4, TOK><<<blocks, kThreads, 0, s>>>(hc, a, ch);
   else if (a.row_bytes % 4 == 0)
-    k_hash_gather<uint32_t><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+    k_hash_gather<uint32_t, TOK><<<blocks, kThreads, 0, s>>>(hc, a, ch);
   else
-    k_hash_gather<uint16_t><<<blocks, kThreads, 0, s>>>(hc, a, ch);
+    k_hash_gather<uint16_t, TOK><<<blocks, kThreads, 0, s>>>(hc, a, ch);
   return hipGetLastError();
+}
+
+hipError_t launch_hash_gather(const HashConsts& hc, const GatherArgs& a, bool compute_hash, hipStream_t s,
+                              int max_blocks) {
+  const int64_t N = (int64_t)a.batch * a.seqlen;
+  if (N == 0) return hipSuccess;
+  if (max_blocks > 0) return hash_gather_tok<kTokens>(hc, a, compute_hash, s, max_blocks);
+  // the most tokens per workgroup that still leaves two workgroups per CU
+  // (a decode step of 256 sequences: one token each; measured on MI355X, B=256
+  // decode 7.4 -> 5.9 us, B=4 T=1024 8.3 -> 7.8 us)
+  if (N >= 16 * 512) return hash_gather_tok<16>(hc, a, compute_hash, s, 0);
+  if (N >= 8 * 512) return hash_gather_tok<8>(hc, a, compute_hash, s, 0);
+  if (N >= 4 * 512) return hash_gather_tok<4>(hc, a, compute_hash, s, 0);
+  if (N >= 2 * 512) return hash_gather_tok<2>(hc, a, compute_hash, s, 0);
+  return hash_gather_tok<1>(hc, a, compute_hash, s, 0);
 }
 
 }  // namespace engram

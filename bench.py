@@ -51,8 +51,11 @@ def kernel_model(w, N, split=False, with_state=False):
         "gate_finalize": {"flops": 0, "bytes": N * hc * (16 * P + 4)},
         "short_conv": {"flops": 0, "bytes": N * (d * s + 4 * hc + hc * d * s) + ring},
         "advance_state": {"flops": 0, "bytes": ring},
+        # one decode step: the partial sums, the value row, the K-1 history taps of
+        # the rings and the new slot written, the output, the taps' weights, and
+        # n_past / the token ring
         "decode_tail": {"flops": 0, "bytes": N * hc * (16 * P) + N * d * s + N * hc * d * s + hc * d * K * s
-                        + 2 * ring},
+                        + K * N * (d * s + 4 * hc) + N * 28},
     }
 
 

@@ -334,51 +334,56 @@ __global__ void __launch_bounds__(256) k_advance(AdvanceArgs a) {
 }
 
 // One decode step (T = 1) with a state, after the fused projection.  Block
-// (channel block cb, sequence b): threads over (branch, 8 channels) as in
-// k_conv.  The gates of the branches the block spans come from the partial
-// sums (8 lanes each, as gate_finalize); the output is the conv over the
-// rings' history with k_conv's arithmetic; then the new position enters the
-// rings at slot past % R.  The rings hold R = (K-1) D + 1 positions, so that
-// slot is never one the history reads (those are past - m D, 0 < m D < R),
-// and the block may write it while other blocks still read the history.
-// Every block reads n_past from the hash kernel's snapshot; one thread then
-// advances n_past and the token ring.
+// (channel block cb, sequence b) of hc wavefronts: wavefront h takes branch h
+// of 64 groups of 8 channels, so the branches of the same channels run on one
+// CU and their reads of the value row and its history taps are served once
+// from memory (branches in other workgroups would land on other XCDs and
+// fetch them again).  The gates of all branches come from the partial sums (8
+// lanes each, as gate_finalize); the output is the conv over the rings'
+// history with k_conv's arithmetic; then the new position enters the rings at
+// slot past % R.  The rings hold R = (K-1) D + 1 positions, so that slot is
+// never one the history reads (those are past - m D, 0 < m D < R), and the
+// block may write it while other blocks still read the history.  Every block
+// reads n_past from the hash kernel's snapshot; one thread then advances
+// n_past and the token ring.
 template <bool BF16, int KS>
-__global__ void __launch_bounds__(256) k_decode_tail(DecodeTailArgs a) {
+__global__ void __launch_bounds__(64 * ENGRAM_MAX_BRANCHES) k_decode_tail(DecodeTailArgs a) {
   __shared__ float sg[ENGRAM_MAX_BRANCHES];
   const int cb = blockIdx.x, b = blockIdx.y;
-  const int groups = a.d >> 3;
-  const int gx = cb * 256 + threadIdx.x;
-  const bool active = gx < a.hc * groups;
-  const int h = active ? gx / groups : 0;
-  const int c0 = (gx - h * groups) * 8;
-  const int h_lo = cb * 256 / groups;
-  const int nb = min(a.hc - 1, (cb * 256 + 255) / groups) - h_lo + 1;
+  const int h = threadIdx.x >> 6;
+  const int gx = cb * 64 + (threadIdx.x & 63);   // 8-channel group of this lane
+  const bool active = gx < (a.d >> 3);
+  const int c0 = gx * 8;
   const int64_t past = a.past[b];
   const int64_t d = a.d, R = a.ring_len;
   const int64_t new_slot = (int64_t)b * R + past % R;
 
-  if ((int)threadIdx.x < 8 * nb) {   // whole 8-lane groups
-    const int hb = threadIdx.x >> 3, hh = h_lo + hb;
-    const float g = gate_from_partials8(a.partials + ((int64_t)b * a.hc + hh) * a.n_part, a.n_part, true, a.d,
-                                        a.eps, a.clamp, a.inv_sqrt_d);
+  if ((int)threadIdx.x < 8 * a.hc) {   // one 8-lane group per branch
+    const int hh = threadIdx.x >> 3;
+    const float g = gate_from_partials8(a.partials + ((int64_t)b * a.hc + hh) * a.n_part, a.n_part, true, a.d, a.eps,
+                                        a.clamp, a.inv_sqrt_d);
     if ((threadIdx.x & 7) == 0) {
-      sg[hb] = g;
-      if (cb == hh * groups / 256) a.g_ring[new_slot * a.hc + hh] = g;   // the block with the branch's first channels
+      sg[hh] = g;
+      if (cb == 0) a.g_ring[new_slot * a.hc + hh] = g;
     }
   }
   __syncthreads();
   if (active) {
-    const float g = sg[h - h_lo];
+    // taps of channels c0..c0+7: conv_w[h][c0+i][0..KS), 8 KS consecutive
+    // elements, loaded 4 at a time (c0 % 8 == 0 keeps every load aligned)
     float w[KS][8];
+    const int64_t e0 = ((int64_t)h * d + c0) * KS;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int q = 0; q < 2 * KS; q++) {
+      float f[4];
+      unpack4<BF16>(*(const Raw4<BF16>*)((const char*)a.conv_w + (e0 + 4 * q) * (BF16 ? 2 : 4)), 1.f, f);
 #pragma unroll
-      for (int j = 0; j < KS; j++) w[j][i] = ld_elem(a.conv_w, ((int64_t)h * d + c0 + i) * KS + j, BF16);
+      for (int m = 0; m < 4; m++) w[(4 * q + m) % KS][(4 * q + m) / KS] = f[m];
+    }
     u32x4 lo, hi = u32x4{0, 0, 0, 0};
     load_raw8<BF16>(a.v, (int64_t)b * d + c0, lo, hi);
     float cur[8];
-    unpack8<BF16>(lo, hi, g, cur);
+    unpack8<BF16>(lo, hi, sg[h], cur);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = fmaf(w[KS - 1][i], cur[i], cur[i]);
@@ -399,7 +404,7 @@ __global__ void __launch_bounds__(256) k_decode_tail(DecodeTailArgs a) {
       for (int i = 0; i < 8; i++) acc[i] = fmaf(w[j][i], hv[i], acc[i]);
     }
     store8(a.out, ((int64_t)b * a.hc + h) * d + c0, BF16, acc);
-    if (h == 0) {   // the value row enters the ring (branch 0's threads cover every channel once)
+    if (h == 0) {   // the value row enters the ring (branch 0's lanes cover every channel once)
       if constexpr (BF16) {
         *(u32x4*)((uint16_t*)a.v_ring + new_slot * d + c0) = lo;
       } else {
@@ -422,14 +427,14 @@ __global__ void __launch_bounds__(256) k_decode_tail(DecodeTailArgs a) {
 template <bool BF16>
 hipError_t decode_tail_dispatch(const DecodeTailArgs& a, dim3 grid, hipStream_t s) {
   switch (a.ksize) {
-    case 1: k_decode_tail<BF16, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_decode_tail<BF16, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_decode_tail<BF16, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: k_decode_tail<BF16, 4><<<grid, 256, 0, s>>>(a); break;
-    case 5: k_decode_tail<BF16, 5><<<grid, 256, 0, s>>>(a); break;
-    case 6: k_decode_tail<BF16, 6><<<grid, 256, 0, s>>>(a); break;
-    case 7: k_decode_tail<BF16, 7><<<grid, 256, 0, s>>>(a); break;
-    case 8: k_decode_tail<BF16, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_decode_tail<BF16, 1><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 2: k_decode_tail<BF16, 2><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 3: k_decode_tail<BF16, 3><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 4: k_decode_tail<BF16, 4><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 5: k_decode_tail<BF16, 5><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 6: k_decode_tail<BF16, 6><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 7: k_decode_tail<BF16, 7><<<grid, 64 * a.hc, 0, s>>>(a); break;
+    case 8: k_decode_tail<BF16, 8><<<grid, 64 * a.hc, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -481,7 +486,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
 hipError_t launch_decode_tail(const DecodeTailArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   if (a.ring_len < 1) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.hc * (a.d / 8) + 255) / 256), (unsigned)a.batch);
+  dim3 grid((unsigned)((a.d / 8 + 63) / 64), (unsigned)a.batch);
   return a.bf16 ? decode_tail_dispatch<true>(a, grid, s) : decode_tail_dispatch<false>(a, grid, s);
 }
 

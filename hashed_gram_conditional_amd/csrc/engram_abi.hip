@@ -245,6 +245,8 @@ struct BwdWorkspace {
   uint32_t* bits;   // row-sparse table gradient: [sparse_bitmap_words] bitmap of the rows used
   uint32_t* count;  // [sparse_groups] set bits per group of the bitmap
   uint32_t* first;  // [sparse_groups] first rank of each group
+  uint32_t* bsum;   // [sparse_scan_blocks] block offsets of the group ranks
+  uint32_t* wrank;  // [sparse_bitmap_words] first rank of each bitmap word
   uint32_t* rank;   // [N][H] rank of each pair's row
   int64_t Np;       // S chunks of Ks tokens (multiples of 64), zero past N
   int64_t Ks;
@@ -310,6 +312,8 @@ BwdWorkspace carve_bwd(const engram_config* c, void* base) {
   w.bits = (uint32_t*)take((size_t)sparse_bitmap_words(rows) * sizeof(uint32_t));
   w.count = (uint32_t*)take((size_t)sparse_groups(rows) * sizeof(uint32_t));
   w.first = (uint32_t*)take((size_t)sparse_groups(rows) * sizeof(uint32_t));
+  w.bsum = (uint32_t*)take((size_t)sparse_scan_blocks(rows) * sizeof(uint32_t));
+  w.wrank = (uint32_t*)take((size_t)sparse_bitmap_words(rows) * sizeof(uint32_t));
   w.rank = (uint32_t*)take((size_t)N * n_heads(c) * sizeof(uint32_t));
   w.bytes = off;
   return w;
@@ -749,6 +753,8 @@ engram_status gradients(const engram_config* cfg, const engram_params* prm, cons
     sa.bits = w.bits;
     sa.count = w.count;
     sa.first = w.first;
+    sa.bsum = w.bsum;
+    sa.wrank = w.wrank;
     sa.pair_rank = w.rank;
     sa.row_index = sp->row_index;
     sa.d_rows = sp->d_rows;

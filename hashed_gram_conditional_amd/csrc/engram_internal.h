@@ -300,6 +300,8 @@ struct SparseRowsArgs {
   uint32_t* bits;        // [sparse_bitmap_words] scratch
   uint32_t* count;       // [sparse_groups] scratch
   uint32_t* first;       // [sparse_groups] scratch
+  uint32_t* bsum;        // [sparse_scan_blocks] scratch
+  uint32_t* wrank;       // [sparse_bitmap_words] scratch
   uint32_t* pair_rank;   // [N * H] scratch
   int64_t* row_index;    // [N * H] out: the rows, ascending (the first *n_rows valid)
   float* d_rows;         // [N * H][head_dim] out: their gradients
@@ -307,6 +309,7 @@ struct SparseRowsArgs {
 };
 int64_t sparse_bitmap_words(int64_t table_rows);
 int64_t sparse_groups(int64_t table_rows);
+int64_t sparse_scan_blocks(int64_t table_rows);
 hipError_t launch_sparse_rows(const SparseRowsArgs& a, hipStream_t s);
 
 struct AdvanceArgs {

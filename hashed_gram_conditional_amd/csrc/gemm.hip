@@ -82,8 +82,8 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
 // all-zero steps and the loop is unrolled over the ring, so every stage index
 // is a constant and the compiler can tell the stage being filled from the one
 // being read (it then inserts no wait of its own between them).  Within a step
-// the fragments of slice kk+1 are read, and one slice of the next step's
-// loads issued, while the MFMAs of slice kk run.  With 8 waves (2 per SIMD)
+// the fragments of slice kk+1 are read, and (in the first half of the step)
+// half of the next step's loads issued, while the MFMAs of slice kk run.  With 8 waves (2 per SIMD)
 // one wave's loads and barrier overlap the other wave's MFMAs.
 //
 // GATE = false: the tile is stored to C (bf16).
@@ -174,10 +174,17 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   auto step_voff = [&](int kt) {
     return (kt < nk && kt * BK + dlog * 8 < K) ? dvoff + kt * BK * 2 : kOutOfRange;
   };
-  // loads [P*kPerStep/KK, (P+1)*kPerStep/KK) of a step into stage S
+  // A step's loads go out over the first half of its slices: slice P < KK/2
+  // issues loads [P*kPerStep/(KK/2), (P+1)*kPerStep/(KK/2)) into stage S.
+  // Spread over all four slices, the last quarter had almost no time to land
+  // before the next step's wait; all in the first slice, they queued behind
+  // its fragment reads (measured on MI355X, 32768 x 20480 x 1920: 2393 / 2301
+  // / 2216 us for four / one / two slices).
+  constexpr int kDmaSlices = KK / 2 > 0 ? KK / 2 : 1;
   auto issue_part = [&](auto stage_tag, int voff, auto part_tag) {
     constexpr int P = decltype(part_tag)::value;
-    constexpr int lo = P * kPerStep / KK, hi = (P + 1) * kPerStep / KK;
+    constexpr int lo = P < kDmaSlices ? P * kPerStep / kDmaSlices : kPerStep;
+    constexpr int hi = P < kDmaSlices ? (P + 1) * kPerStep / kDmaSlices : kPerStep;
     [&]<int... X>(std::integer_sequence<int, X...>) {
       (issue_one(stage_tag, voff, std::integral_constant<int, lo + X>{}), ...);
     }(std::make_integer_sequence<int, hi - lo>{});
@@ -255,7 +262,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   };
   auto issue_q_part = [&](auto part_tag) {
     constexpr int P = decltype(part_tag)::value;
-    constexpr int lo = P * kPerStep / KK, hi = (P + 1) * kPerStep / KK;
+    constexpr int lo = P < kDmaSlices ? P * kPerStep / kDmaSlices : kPerStep;
+    constexpr int hi = P < kDmaSlices ? (P + 1) * kPerStep / kDmaSlices : kPerStep;
     [&]<int... X>(std::integer_sequence<int, X...>) {
       (issue_q_one(std::integral_constant<int, lo + X>{}), ...);
     }(std::make_integer_sequence<int, hi - lo>{});

@@ -361,6 +361,26 @@ def test_chunks_with_every_count_at_its_maximum_match_single_prefill(eg):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("hc,hidden", [(1, 128), (3, 256), (16, 128)])
+def test_decode_steps_with_any_branch_count_match_single_prefill(eg, hc, hidden):
+    """Single-token steps run decode_tail, whose workgroups hold one wavefront
+    per branch (64 to 1024 threads): 1, 3 and 16 branches, bit-equal to one
+    prefill over the same tokens."""
+    c = case("b4_t1024", batch=3, seqlen=24, hidden=hidden, hc_mult=hc)
+    assert eg.kernel_names(c.cfg(c.B, 1), with_state=True)[-1] == "decode_tail"
+    full = eg.forward(c.cfg(), c.params, c.dev["ids"], c.dev["hidden"])
+    st = eg.State(c.cfg(), c.B)
+    outs, t0 = [], 0
+    for L in (5, 1, 1, 1, 3, 1, 1, 1, 1, 1, 1, 7):
+        ids = c.dev["ids"][:, t0:t0 + L].contiguous()
+        hid = c.dev["hidden"][:, t0:t0 + L].contiguous()
+        outs.append(eg.forward(c.cfg(c.B, L), c.params, ids, hid, state=st))
+        t0 += L
+    sync()
+    assert t0 == c.T
+    assert torch.equal(torch.cat(outs, dim=1), full)
+
+
 def test_long_chunks_match_single_prefill(eg):
     """Chunks of more than 16384 tokens each take the conv's long walks, whose
     history at the chunk start comes from the state's rings; T = 2100 leaves a

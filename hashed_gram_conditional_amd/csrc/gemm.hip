@@ -174,13 +174,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_gemm_bf16(GemmGateArgs ga) 
   auto step_voff = [&](int kt) {
     return (kt < nk && kt * BK + dlog * 8 < K) ? dvoff + kt * BK * 2 : kOutOfRange;
   };
-  // A step's loads go out over the first half of its slices: slice P < KK/2
-  // issues loads [P*kPerStep/(KK/2), (P+1)*kPerStep/(KK/2)) into stage S.
-  // Spread over all four slices, the last quarter had almost no time to land
-  // before the next step's wait; all in the first slice, they queued behind
-  // its fragment reads (measured on MI355X, 32768 x 20480 x 1920: 2393 / 2301
-  // / 2216 us for four / one / two slices).
-  constexpr int kDmaSlices = KK / 2 > 0 ? KK / 2 : 1;
+  // With two stages a step's loads go out over the first half of its slices:
+  // slice P < KK/2 issues loads [P*kPerStep/(KK/2), (P+1)*kPerStep/(KK/2))
+  // into stage S.  Spread over all four slices, the last quarter had almost
+  // no time to land before the next step's wait; all in the first slice, they
+  // queued behind its fragment reads (measured on MI355X, 32768 x 20480 x
+  // 1920: 2393 / 2301 / 2216 us for four / one / two slices).  With four
+  // stages the loads have three steps to land and go out over all four slices
+  // (256 x 12800 x 1024 with the gate: 14.6 -> 14.1 us).
+  constexpr int kDmaSlices = kStages > 2 ? KK : (KK / 2 > 0 ? KK / 2 : 1);
   auto issue_part = [&](auto stage_tag, int voff, auto part_tag) {
     constexpr int P = decltype(part_tag)::value;
     constexpr int lo = P < kDmaSlices ? P * kPerStep / kDmaSlices : kPerStep;

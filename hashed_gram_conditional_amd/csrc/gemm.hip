@@ -580,43 +580,54 @@ __global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
   }
 }
 
-// float32 path: a plain LDS-tiled FMA GEMM, 64x64 tile, 4x4 outputs per thread.
-constexpr int FT = 64, FK = 16;
+// float32 path: v_mfma_f32_32x32x2_f32 with float32 accumulation.  A 64x64
+// tile per workgroup of 4 waves, each wave one 32x32 block; K steps of 32
+// staged through LDS (rows padded by one float).  As in the bf16 kernel the
+// MFMA "A" operand is the weight rows and "B" the token rows: lane l supplies
+// row l % 32 at k = l / 32 of each pair of k, and accumulator r holds channel
+// 8 (r/4) + 4 (l/32) + r%4 of token l % 32 of the wave's block.
+constexpr int FT = 64, FK = 32;
 
 __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
-  __shared__ float sA[FK][FT + 1];
-  __shared__ float sB[FK][FT + 1];
+  __shared__ float sA[FT][FK + 1];   // token rows x k
+  __shared__ float sB[FT][FK + 1];   // weight rows x k
   const float* __restrict__ A = (const float*)a.A;
   const float* __restrict__ B = (const float*)a.B;
   float* __restrict__ C = (float*)a.C;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.y * FT, n0 = (int64_t)blockIdx.x * FT;
-  float acc[4][4] = {};
+  const int row = lane & 31, kh = lane >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; r++) acc[r] = 0.f;
   for (int k0 = 0; k0 < a.K; k0 += FK) {
-    for (int i = threadIdx.x; i < FT * FK; i += 256) {
+    for (int i = tid; i < FT * FK; i += 256) {
       const int r = i / FK, kk = i % FK;
       const int64_t m = m0 + r, n = n0 + r;
       const int k = k0 + kk;
-      sA[kk][r] = (m < a.M && k < a.K) ? A[m * a.K + k] : 0.f;
-      sB[kk][r] = (n < a.N && k < a.K) ? B[n * a.K + k] : 0.f;
+      sA[r][kk] = (m < a.M && k < a.K) ? A[m * a.K + k] : 0.f;
+      sB[r][kk] = (n < a.N && k < a.K) ? B[n * a.K + k] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < FK; kk++)
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = fmaf(sA[kk][ty * 4 + i], sB[kk][tx * 4 + j], acc[i][j]);
+    for (int kk = 0; kk < FK; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sB[wn * 32 + row][kk + kh], sA[wm * 32 + row][kk + kh], acc, 0, 0,
+                                                 0);
     __syncthreads();
   }
-  for (int i = 0; i < 4; i++) {
-    const int64_t m = m0 + ty * 4 + i;
-    if (m >= a.M) continue;
-    for (int j = 0; j < 4; j++) {
-      const int64_t n = n0 + tx * 4 + j;
-      if (n < a.N) C[m * a.N + n] = a.accumulate ? C[m * a.N + n] + acc[i][j] : acc[i][j];
+  const int64_t m = m0 + wm * 32 + row;
+  if (m >= a.M) return;
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int64_t n = n0 + wn * 32 + 8 * q + 4 * kh + e;
+      if (n < a.N) {
+        float* c = C + m * a.N + n;
+        *c = a.accumulate ? *c + acc[4 * q + e] : acc[4 * q + e];
+      }
     }
-  }
 }
 
 }  // namespace

@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Engram forward tokens/sec at 1 MI355X; gather/gate HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+FP32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 on the matrix cores (v_mfma_f32_32x32x2_f32)
 
 
 def kernel_model(w, N, split=False, with_state=False):
@@ -77,7 +77,7 @@ def roofline_of(work, us, dtype):
     t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
     if work["flops"] and t_mfma >= t_hbm:
         ach = work["flops"] / (us * 1e-6) / 1e12
-        return {"bound": "mfma" if dtype == "bf16" else "alu", "achieved": round(ach, 1), "peak": mfma_peak,
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(ach / mfma_peak, 4), "work_per_launch": work["flops"]}
     ach = work["bytes"] / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -580,17 +580,23 @@ __global__ void __launch_bounds__(256) k_gate_finalize(GateFinalizeArgs a) {
   }
 }
 
-// float32 path: v_mfma_f32_32x32x2_f32 with float32 accumulation.  A 64x64
-// tile per workgroup of 4 waves, each wave one 32x32 block; K steps of 32
-// staged through LDS (rows padded by one float).  As in the bf16 kernel the
+// float32 path: v_mfma_f32_32x32x2_f32 with float32 accumulation.  An FT x FT
+// tile per workgroup of 4 waves (FT = 128: each wave 64x64 as 2x2 blocks of
+// 32x32; FT = 64 for small products: one block per wave); K
+// steps of 16 staged through two LDS buffers, stored k-major (a row of 128
+// tile rows per k, padded by 32 floats so that the two k of an MFMA operand
+// fall in different bank halves), with the next step's global loads in
+// registers while the current one is multiplied.  As in the bf16 kernel the
 // MFMA "A" operand is the weight rows and "B" the token rows: lane l supplies
 // row l % 32 at k = l / 32 of each pair of k, and accumulator r holds channel
-// 8 (r/4) + 4 (l/32) + r%4 of token l % 32 of the wave's block.
-constexpr int FT = 64, FK = 32;
+// 8 (r/4) + 4 (l/32) + r%4 of token l % 32 of its block.
+constexpr int FK = 16;
 
+template <int FT, bool VEC>
 __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
-  __shared__ float sA[FT][FK + 1];   // token rows x k
-  __shared__ float sB[FT][FK + 1];   // weight rows x k
+  constexpr int FP = FT + 32, NB = FT / 64, H = FT * 4 / 256;
+  __shared__ float sA[2][FK][FP];   // k x token rows
+  __shared__ float sB[2][FK][FP];   // k x weight rows
   const float* __restrict__ A = (const float*)a.A;
   const float* __restrict__ B = (const float*)a.B;
   float* __restrict__ C = (float*)a.C;
@@ -598,36 +604,86 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.y * FT, n0 = (int64_t)blockIdx.x * FT;
   const int row = lane & 31, kh = lane >> 5;
-  f32x16 acc;
+  const int K = a.K, nk = (K + FK - 1) / FK;
+  // this thread's share of a step: H runs of 4 k of one row per operand
+  // (float4 index x: row x / 4, k 4 (x % 4)), tid, tid + 256, ...
+  float ra[H][4], rb[H][4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int r = 0; r < 16; r++) acc[r] = 0.f;
-  for (int k0 = 0; k0 < a.K; k0 += FK) {
-    for (int i = tid; i < FT * FK; i += 256) {
-      const int r = i / FK, kk = i % FK;
+    for (int h = 0; h < H; h++) {
+      const int x = tid + 256 * h, r = x >> 2, k = k0 + 4 * (x & 3);
       const int64_t m = m0 + r, n = n0 + r;
-      const int k = k0 + kk;
-      sA[r][kk] = (m < a.M && k < a.K) ? A[m * a.K + k] : 0.f;
-      sB[r][kk] = (n < a.N && k < a.K) ? B[n * a.K + k] : 0.f;
-    }
-    __syncthreads();
+      if constexpr (VEC) {
+        const float4 va = (m < a.M && k < K) ? *(const float4*)(A + m * K + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 vb = (n < a.N && k < K) ? *(const float4*)(B + n * K + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[h][0] = va.x, ra[h][1] = va.y, ra[h][2] = va.z, ra[h][3] = va.w;
+        rb[h][0] = vb.x, rb[h][1] = vb.y, rb[h][2] = vb.z, rb[h][3] = vb.w;
+      } else {
 #pragma unroll
-    for (int kk = 0; kk < FK; kk += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sB[wn * 32 + row][kk + kh], sA[wm * 32 + row][kk + kh], acc, 0, 0,
-                                                 0);
-    __syncthreads();
-  }
-  const int64_t m = m0 + wm * 32 + row;
-  if (m >= a.M) return;
-#pragma unroll
-  for (int q = 0; q < 4; q++)
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int64_t n = n0 + wn * 32 + 8 * q + 4 * kh + e;
-      if (n < a.N) {
-        float* c = C + m * a.N + n;
-        *c = a.accumulate ? *c + acc[4 * q + e] : acc[4 * q + e];
+        for (int e = 0; e < 4; e++) {
+          ra[h][e] = (m < a.M && k + e < K) ? A[m * K + k + e] : 0.f;
+          rb[h][e] = (n < a.N && k + e < K) ? B[n * K + k + e] : 0.f;
+        }
       }
     }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < H; h++) {
+      const int x = tid + 256 * h, r = x >> 2, k = 4 * (x & 3);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        sA[buf][k + e][r] = ra[h][e];
+        sB[buf][k + e][r] = rb[h][e];
+      }
+    }
+  };
+  f32x16 acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; i++)
+#pragma unroll
+    for (int j = 0; j < NB; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) fetch((kt + 1) * FK);
+#pragma unroll
+    for (int kk = 0; kk < FK; kk += 2) {
+      float fa[NB], fb[NB];
+#pragma unroll
+      for (int i = 0; i < NB; i++) fa[i] = sB[cur][kk + kh][wn * (FT / 2) + i * 32 + row];
+#pragma unroll
+      for (int j = 0; j < NB; j++) fb[j] = sA[cur][kk + kh][wm * (FT / 2) + j * 32 + row];
+#pragma unroll
+      for (int i = 0; i < NB; i++)
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) stash(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < NB; j++) {
+    const int64_t m = m0 + wm * (FT / 2) + j * 32 + row;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int i = 0; i < NB; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int64_t n = n0 + wn * (FT / 2) + i * 32 + 8 * q + 4 * kh + e;
+          if (n < a.N) {
+            float* c = C + m * a.N + n;
+            *c = a.accumulate ? *c + acc[i][j][4 * q + e] : acc[i][j][4 * q + e];
+          }
+        }
+  }
 }
 
 }  // namespace
@@ -747,8 +803,15 @@ hipError_t launch_gate_finalize(const GateFinalizeArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  dim3 grid((a.N + FT - 1) / FT, (a.M + FT - 1) / FT);
-  k_gemm_f32<<<grid, 256, 0, s>>>(a);
+  // float4 loads need every row 16-byte aligned; 64-wide tiles while the
+  // 128-wide ones would not give every CU one
+  const bool vec = a.K % 4 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0;
+  const bool big = ((int64_t)(a.M + 127) / 128) * ((a.N + 127) / 128) >= 256;
+  const dim3 grid64((a.N + 63) / 64, (a.M + 63) / 64), grid128((a.N + 127) / 128, (a.M + 127) / 128);
+  if (big && vec) k_gemm_f32<128, true><<<grid128, 256, 0, s>>>(a);
+  else if (big) k_gemm_f32<128, false><<<grid128, 256, 0, s>>>(a);
+  else if (vec) k_gemm_f32<64, true><<<grid64, 256, 0, s>>>(a);
+  else k_gemm_f32<64, false><<<grid64, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
